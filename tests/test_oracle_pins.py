@@ -1,0 +1,404 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin ties a part of the oracle to the mathematics or to an independent
+route: a closed form worked by hand, a special case that reduces to a library
+routine (torch, not numpy), brute force over all subsets on tiny inputs, and
+exact invariants.  The last section plants mistakes in the oracle and checks
+that some pin catches each of them.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prox_oracle as O
+from prox_workloads import bf16_round, bf16_to_f32, gen_small, gen_ties
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _f64(bits):
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+def _case(d, F, B, seed, kind="small"):
+    c = gen_small(d, F, B, seed) if kind == "small" else gen_ties(d, F, B, seed)
+    return _f64(c["x"]), _f64(c["wg_t"]), _f64(c["wu_t"]), _f64(c["wd"])
+
+
+# ---------------------------------------------------------------------------
+# P1. With every channel kept (k_ff = F) the method is the dense SwiGLU FFN
+# (PrunePath, §2.1, Eq. (1); all units active recovers the dense FFN, §2.2,
+# Eq. (2)).  Reference: torch float64 silu/linear, not the oracle's numpy.
+# ---------------------------------------------------------------------------
+
+def _torch_dense(x, wg_t, wu_t, wd):
+    X, G, U, D = (torch.from_numpy(a) for a in (x, wg_t, wu_t, wd))
+    h = torch.nn.functional.silu(torch.nn.functional.linear(X, G)) * torch.nn.functional.linear(X, U)
+    return (h @ D).numpy()
+
+
+def check_dense_identity(kind, d, F, B, k_in, seed):
+    x, wg, wu, wd = _case(d, F, B, seed)
+    y = O.oracle_forward(x, wg, wu, wd, kind, k_in, F).y
+    ref = _torch_dense(x, wg, wu, wd)
+    scale = np.max(np.abs(ref))
+    assert np.max(np.abs(y - ref)) <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("kind", ["int8", "int4", "exact"])
+@pytest.mark.parametrize("k_in_frac", [0.0, 0.5, 1.0])
+def test_p1_dense_identity(kind, k_in_frac):
+    d, F = 256, 96
+    check_dense_identity(kind, d, F, 3, int(d * k_in_frac), seed=11)
+
+
+# ---------------------------------------------------------------------------
+# P2. Exact proxy (W~ = W) and no input sparsity: the mask is the top-k of the
+# dense |h| (Prox, Abstract: the mask is the one the intermediate induces).
+# Reference: torch stable descending sort of the float64 |h| from torch.
+# Channels whose |h| lies within fp32 rounding (2^-23 relative) of the k-th
+# value may be ordered differently by the fp32 ranking key, and are excused.
+# ---------------------------------------------------------------------------
+
+def check_exact_mask(d, F, k_ff, seed, kind="small"):
+    x, wg, wu, wd = _case(d, F, 2, seed, kind)
+    res = O.oracle_forward(x, wg, wu, wd, "exact", d, k_ff)
+    X, G, U = (torch.from_numpy(a) for a in (x, wg, wu))
+    h = torch.nn.functional.silu(X @ G.T) * (X @ U.T)
+    for b, tok in enumerate(res.tokens):
+        hb = h[b].abs()
+        order = torch.sort(hb, descending=True, stable=True).indices[:k_ff]
+        ref = set(order.tolist())
+        got = set(tok.mask.tolist())
+        if k_ff == 0:
+            assert got == set()
+            continue
+        t = float(hb[order[-1]])
+        for j in ref ^ got:
+            assert abs(float(hb[j]) - t) <= 2.0 ** -23 * t, (j, float(hb[j]), t)
+
+
+@pytest.mark.parametrize("k_ff", [0, 1, 17, 48, 95, 96])
+def test_p2_exact_proxy_mask(k_ff):
+    check_exact_mask(128, 96, k_ff, seed=5)
+
+
+def test_p2_exact_proxy_mask_ties():
+    # dyadic weights/inputs: many exactly equal |h|; ties go to the lower index
+    check_exact_mask(16, 64, 20, seed=3, kind="ties")
+
+
+# ---------------------------------------------------------------------------
+# P3. Brute force on tiny inputs: every subset of the right size is tried;
+# exactly one dominates all outside it (|v| larger, or equal and lower
+# index).  Scores and y by scalar loops with exactly rounded sums (fsum).
+# ---------------------------------------------------------------------------
+
+def _brute_select(vals, k):
+    n = len(vals)
+    winners = []
+    for S in itertools.combinations(range(n), k):
+        inside, ok = set(S), True
+        for j in S:
+            for jj in range(n):
+                if jj in inside:
+                    continue
+                if not (abs(vals[j]) > abs(vals[jj]) or (abs(vals[j]) == abs(vals[jj]) and j < jj)):
+                    ok = False
+                    break
+            if not ok:
+                break
+        if ok:
+            winners.append(S)
+    assert len(winners) == 1
+    return list(winners[0])
+
+
+def _silu_scalar(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def check_brute_force(d, F, k_in, k_ff, kind, seed, data="small"):
+    x, wg, wu, wd = _case(d, F, 1, seed, data)
+    x = x[0]
+    res = O.oracle_forward(x[None], wg, wu, wd, kind, k_in, k_ff)
+    tok = res.tokens[0]
+    # independent proxy values: scalar s * q (or the weight itself)
+    pg, pu = O.build_proxy(wg.T, kind), O.build_proxy(wu.T, kind)
+
+    def wtil(p, w_t, i, j):
+        if kind == "exact":
+            return float(w_t[j, i])
+        s = p.s[j] if kind == "int8" else p.s[i // 128, j]
+        return float(s) * float(p.q[i, j])
+
+    s_in = _brute_select([float(v) for v in x], k_in)
+    assert list(tok.s_in) == s_in
+    keys = []
+    for j in range(F):
+        gh = math.fsum(float(x[i]) * wtil(pg, wg, i, j) for i in s_in)
+        uh = math.fsum(float(x[i]) * wtil(pu, wu, i, j) for i in s_in)
+        hh = _silu_scalar(gh) * uh
+        assert abs(hh - tok.h_hat[j]) <= 1e-13 * max(1e-300, abs(hh)) + 1e-300
+        keys.append(float(np.float32(abs(hh))))
+    m = _brute_select(keys, k_ff)
+    assert list(tok.mask) == m
+    y = []
+    for c in range(d):
+        terms = []
+        for j in m:
+            g = math.fsum(float(x[i]) * float(wg[j, i]) for i in range(d))
+            u = math.fsum(float(x[i]) * float(wu[j, i]) for i in range(d))
+            terms.append(_silu_scalar(g) * u * float(wd[j, c]))
+        y.append(math.fsum(terms))
+    y = np.array(y)
+    scale = max(np.max(np.abs(y)), 1e-300)
+    assert np.max(np.abs(tok.y - y)) <= 1e-12 * scale
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("kind", ["int8", "exact"])
+def test_p3_brute_force_random(seed, kind):
+    check_brute_force(10, 9, 5, 4, kind, seed)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_p3_brute_force_ties(seed):
+    # tie-heavy data exercises "lower index wins" in both selections
+    check_brute_force(10, 10, 4, 5, "int8", seed, data="ties")
+
+
+def test_p3_brute_force_int4():
+    # int4 needs d = 128; brute force over the channel subsets only (F small)
+    x, wg, wu, wd = _case(128, 8, 1, 21)
+    res = O.oracle_forward(x, wg, wu, wd, "int4", 77, 3)
+    tok = res.tokens[0]
+    pg, pu = O.build_proxy(wg.T, "int4"), O.build_proxy(wu.T, "int4")
+    order = sorted(range(128), key=lambda i: (-abs(x[0, i]), i))[:77]
+    assert list(tok.s_in) == sorted(order)
+    keys = []
+    for j in range(8):
+        gh = math.fsum(float(x[0, i]) * float(pg.s[0, j]) * float(pg.q[i, j]) for i in order)
+        uh = math.fsum(float(x[0, i]) * float(pu.s[0, j]) * float(pu.q[i, j]) for i in order)
+        keys.append(float(np.float32(abs(_silu_scalar(gh) * uh))))
+    assert list(tok.mask) == _brute_select(keys, 3)
+
+
+# ---------------------------------------------------------------------------
+# P4. Quantiser: worked values and invariants.
+# ---------------------------------------------------------------------------
+
+def test_p4_int8_worked_values():
+    # column max 127 * 2^-7 gives s = 2^-7 exactly, so codes are w * 2^7;
+    # the half-way codes 2.5, 3.5, -2.5 round to even: 2, 4, -2.
+    col = np.array([127, -64, 3, 0, -127, 1, 2.5, 3.5, -2.5], dtype=np.float64) / 128.0
+    q, s = O.quantize_int8_pc(col[:, None])
+    assert s[0] == np.float32(2.0 ** -7)
+    assert q[:, 0].tolist() == [127, -64, 3, 0, -127, 1, 2, 4, -2]
+
+
+def test_p4_int4_worked_values():
+    g0 = np.zeros(128)
+    g0[:6] = np.array([7, -3, 2.5, 1.5, -0.5, 0.25]) / 8.0     # max 7/8 -> s = 1/8
+    g1 = np.zeros(128)
+    g1[0] = -0.4375                                           # max 7/16 -> s = 1/16
+    g1[1] = 0.09375                                           # 1.5 -> 2
+    q, s = O.quantize_int4_g128(np.concatenate([g0, g1])[:, None])
+    assert s[:, 0].tolist() == [0.125, 0.0625]
+    assert q[:6, 0].tolist() == [7, -3, 2, 2, 0, 0]
+    assert q[128:130, 0].tolist() == [-7, 2]
+
+
+def test_p4_zero_column():
+    w = np.zeros((256, 3))
+    w[:, 1] = 0.5
+    q, s = O.quantize_int8_pc(w)
+    assert s[0] == 0 and s[2] == 0 and not q[:, 0].any() and not q[:, 2].any()
+    q4, s4 = O.quantize_int4_g128(w)
+    assert not q4[:, 0].any() and (s4[:, 0] == 0).all()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_p4_invariants(seed):
+    _, wg, _, _ = _case(256, 64, 1, seed)
+    w = wg.T
+    for kind, qmax in (("int8", 127), ("int4", 7)):
+        p = O.build_proxy(w, kind)
+        assert np.abs(p.q).max() <= qmax
+        if kind == "int8":
+            s_full = np.broadcast_to(p.s[None, :].astype(np.float64), w.shape)
+            assert (np.abs(p.q).max(axis=0) == qmax).all()
+        else:
+            s_full = np.repeat(p.s.astype(np.float64), 128, axis=0)
+            assert (np.abs(p.q.reshape(2, 128, -1)).max(axis=1) == qmax).all()
+        # |w/s - q| <= 1/2 plus the fp32 rounding of w/s (at most qmax * 2^-24)
+        err = np.abs(w - s_full * p.q)
+        assert (err <= s_full * (0.5 + qmax * 2.0 ** -23)).all()
+
+
+# ---------------------------------------------------------------------------
+# P5. Whole-forward invariants.
+# ---------------------------------------------------------------------------
+
+def test_p5_channel_permutation():
+    # permuting channels (columns of W_gate/W_up, rows of W_down; PrunePath,
+    # §2.2) permutes the mask and leaves y unchanged
+    x, wg, wu, wd = _case(256, 128, 2, 9)
+    perm = np.random.default_rng(0).permutation(128)
+    a = O.oracle_forward(x, wg, wu, wd, "int8", 150, 40)
+    b = O.oracle_forward(x, wg[perm], wu[perm], wd[perm], "int8", 150, 40)
+    for ta, tb in zip(a.tokens, b.tokens):
+        assert sorted(perm[tb.mask].tolist()) == ta.mask.tolist()
+    assert np.max(np.abs(a.y - b.y)) <= 1e-12 * np.max(np.abs(a.y))
+
+
+def test_p5_scaling():
+    # ranking only: W_up * 2^e scales h~ and y exactly, the mask is unchanged;
+    # W_down * c scales y only
+    x, wg, wu, wd = _case(256, 128, 2, 10)
+    a = O.oracle_forward(x, wg, wu, wd, "int8", 120, 50)
+    b = O.oracle_forward(x, wg, wu * 4.0, wd, "int8", 120, 50)
+    c = O.oracle_forward(x, wg, wu, wd * 3.0, "int8", 120, 50)
+    for ta, tb, tc in zip(a.tokens, b.tokens, c.tokens):
+        assert ta.mask.tolist() == tb.mask.tolist() == tc.mask.tolist()
+        assert np.array_equal(tb.h_hat, 4.0 * ta.h_hat)
+    assert np.array_equal(b.y, 4.0 * a.y)
+    assert np.max(np.abs(c.y - 3.0 * a.y)) <= 1e-13 * np.max(np.abs(c.y))
+
+
+def test_p5_batch_independence():
+    x, wg, wu, wd = _case(128, 64, 4, 12)
+    a = O.oracle_forward(x, wg, wu, wd, "int8", 64, 20)
+    for b in range(4):
+        s = O.oracle_forward(x[b:b + 1], wg, wu, wd, "int8", 64, 20)
+        assert s.tokens[0].mask.tolist() == a.tokens[b].mask.tolist()
+        assert np.array_equal(s.y[0], a.y[b])
+
+
+def test_p5_nested_masks():
+    x, wg, wu, wd = _case(128, 64, 1, 13, "ties")
+    prev = set()
+    for k in range(65):
+        m = set(O.oracle_forward(x, wg, wu, wd, "int8", 70, k).tokens[0].mask.tolist())
+        assert prev <= m and len(m) == k
+        prev = m
+
+
+def test_p5_edge_cases():
+    x, wg, wu, wd = _case(128, 64, 1, 14)
+    r0 = O.oracle_forward(x, wg, wu, wd, "int8", 64, 0)
+    assert r0.tokens[0].mask.size == 0 and not r0.y.any()
+    # no input kept: every score is 0, so the first k channels win
+    r1 = O.oracle_forward(x, wg, wu, wd, "int8", 0, 10)
+    assert r1.tokens[0].mask.tolist() == list(range(10))
+    assert not r1.tokens[0].h_hat.any()
+    # all inputs kept == the proxy pre-activation over the dense x
+    r2 = O.oracle_forward(x, wg, wu, wd, "int8", 128, 10)
+    pg = O.build_proxy(wg.T, "int8")
+    assert np.allclose(r2.tokens[0].g_hat, x[0] @ pg.w_tilde, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.oracle_forward(x, wg, wu, wd, "int8", 129, 10)
+    with pytest.raises(ValueError):
+        O.oracle_forward(x * np.inf, wg, wu, wd, "int8", 10, 10)
+
+
+# ---------------------------------------------------------------------------
+# P6. A d = 4, F = 4 example worked by hand.
+#
+#   x = [2, -1, 0.5, 4], k_in = 2  ->  S_in = {0, 3}   (|4| > |2| > |-1| > |0.5|)
+#   W_gate = Qg / 128, W_up = Qu / 128 with each column reaching 127, so the
+#   int8 proxy is exact: s_j = 2^-7 and q = Q.
+#   g~_j = (2 Qg[0,j] + 4 Qg[3,j]) / 128 = [246, -4, -60, 2] / 128
+#   u~_j = (2 Qu[0,j] + 4 Qu[3,j]) / 128 = [132, 294, -20, 512] / 128
+#   |h~| = |silu(g~) u~| ~ [1.7289, 0.03533, 0.02819, 0.03149]  ->  M = {0, 1}
+#   exact (dense x): g = [245, -129.5] / 128, u = [5, 291.5] / 128 on M
+#   y = silu(g0) u0 * Wd[0] + silu(g1) u1 * Wd[1]
+# ---------------------------------------------------------------------------
+
+QG = np.array([[127, 0, 10, -127], [1, 127, 0, 5], [0, 3, 127, 0], [-2, -1, -20, 64]], float)
+QU = np.array([[64, 127, -8, 2], [127, 0, 0, 0], [0, -5, 127, 1], [1, 10, -1, 127]], float)
+WD = np.array([[1, 0, -1, 0.5], [0, 2, 0, -1], [3, 3, 3, 3], [-1, 1, -1, 1]], float)
+XH = np.array([[2, -1, 0.5, 4]], float)
+
+
+def test_p6_hand_example():
+    wg_t, wu_t = (QG / 128).T, (QU / 128).T
+    for kind in ("int8", "exact"):
+        tok = O.oracle_forward(XH, wg_t, wu_t, WD, kind, 2, 2).tokens[0]
+        assert tok.s_in.tolist() == [0, 3]
+        assert tok.g_hat.tolist() == [246 / 128, -4 / 128, -60 / 128, 2 / 128]
+        assert tok.u_hat.tolist() == [132 / 128, 294 / 128, -20 / 128, 512 / 128]
+        sil = lambda z: z / (1 + math.exp(-z))  # noqa: E731
+        hh = [sil(a / 128) * b / 128 for a, b in ((246, 132), (-4, 294), (-60, -20), (2, 512))]
+        assert np.allclose(tok.h_hat, hh, rtol=1e-15, atol=0)
+        assert tok.mask.tolist() == [0, 1]
+        h0 = sil(245 / 128) * 5 / 128
+        h1 = sil(-129.5 / 128) * 291.5 / 128
+        y = [h0 * WD[0, c] + h1 * WD[1, c] for c in range(4)]
+        assert np.allclose(tok.y, y, rtol=1e-15, atol=1e-300)
+    q, s = O.quantize_int8_pc(QG / 128)
+    assert (s == np.float32(2.0 ** -7)).all() and np.array_equal(q, QG.astype(np.int8))
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each must be caught by at least one pin above.
+# ---------------------------------------------------------------------------
+
+def _caught(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_mutant_tie_break_reversed(monkeypatch):
+    def bad(keys, k):
+        n = keys.shape[0]
+        order = np.lexsort((-np.arange(n), -np.asarray(keys)))
+        return np.sort(order[:k])
+    monkeypatch.setattr(O, "select_topk", bad)
+    assert _caught(lambda: check_brute_force(10, 10, 4, 5, "int8", 0, data="ties"))
+
+
+def test_mutant_wrong_activation(monkeypatch):
+    monkeypatch.setattr(O, "silu", lambda z: np.asarray(z) / (1.0 + np.exp(np.asarray(z))))
+    assert _caught(lambda: check_dense_identity("int8", 64, 32, 1, 32, 0))
+
+
+def test_mutant_signed_ranking(monkeypatch):
+    orig = O.stage1_token
+
+    def bad(x, pg, pu, k_in, k_ff):
+        s_in, g, u, h, key, mask, t = orig(x, pg, pu, k_in, k_ff)
+        mask = O.select_topk(h.astype(np.float32), k_ff)     # ranks h~, not |h~|
+        return s_in, g, u, h, key, mask, t
+    monkeypatch.setattr(O, "stage1_token", bad)
+    assert _caught(lambda: check_exact_mask(128, 96, 17, 5))
+
+
+def test_mutant_input_sparsity_dropped(monkeypatch):
+    orig = O.stage1_token
+    monkeypatch.setattr(O, "stage1_token", lambda x, pg, pu, k_in, k_ff: orig(x, pg, pu, x.shape[0], k_ff))
+    assert _caught(test_p6_hand_example)
+
+
+def test_mutant_round_half_away(monkeypatch):
+    def bad(w32, amax32, qmax):
+        s = (amax32 / np.float32(qmax)).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = (w32 / s).astype(np.float32)
+        q = np.where(s > 0, np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -qmax, qmax), 0)
+        return q.astype(np.int8), s
+    monkeypatch.setattr(O, "_quantize_block", bad)
+    assert _caught(test_p4_int8_worked_values)
+
+
+def test_mutant_down_transposed(monkeypatch):
+    orig = O.stage2_token
+    monkeypatch.setattr(O, "stage2_token", lambda x, wg, wu, wd, m: orig(x, wg, wu, np.ascontiguousarray(wd.T), m))
+    assert _caught(lambda: check_dense_identity("int8", 64, 64, 1, 32, 0))
