@@ -1,0 +1,353 @@
+// Device helpers shared by the Prox kernels (gfx950, wave64).
+//
+// Block-wide steps here synchronise with lds_barrier(): it waits for this
+// wave's LDS operations only, so global loads issued earlier (prefetched
+// weight rows) stay in flight across the barrier.  No kernel relies on a
+// barrier to order global memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prox {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint32_t v16) { return __uint_as_float(v16 << 16); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Number of set bits of `m` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// ---- cross-lane moves (DPP within rows of 16 lanes, permlane swaps across rows)
+// dpp_ror<n>: lane i receives lane (i + n) mod 16 of its row.
+template <int N>
+__device__ __forceinline__ int dpp_ror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x120 + N, 0xf, 0xf, false); }
+template <int N>
+__device__ __forceinline__ float dpp_ror(float v) { return __int_as_float(dpp_ror<N>(__float_as_int(v))); }
+// sum of the lane pairs (i, i ^ 16) / (i, i ^ 32): permlane swaps with both operands v
+__device__ __forceinline__ int xor16_add(int v) {
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (int)r[0] + (int)r[1];
+}
+__device__ __forceinline__ int xor32_add(int v) {
+    auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (int)r[0] + (int)r[1];
+}
+__device__ __forceinline__ float xor16_add(float v) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_add(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ double dpp_ror8(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int lo = dpp_ror<8>((int)(uint32_t)u), hi = dpp_ror<8>((int)(uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ double xor16_add(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    auto lo = __builtin_amdgcn_permlane16_swap((int)(uint32_t)u, (int)(uint32_t)u, false, false);
+    auto hi = __builtin_amdgcn_permlane16_swap((int)(uint32_t)(u >> 32), (int)(uint32_t)(u >> 32), false, false);
+    const double a = __longlong_as_double((long long)(((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]));
+    const double b = __longlong_as_double((long long)(((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]));
+    return a + b;
+}
+__device__ __forceinline__ double xor32_add(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    auto lo = __builtin_amdgcn_permlane32_swap((int)(uint32_t)u, (int)(uint32_t)u, false, false);
+    auto hi = __builtin_amdgcn_permlane32_swap((int)(uint32_t)(u >> 32), (int)(uint32_t)(u >> 32), false, false);
+    const double a = __longlong_as_double((long long)(((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]));
+    const double b = __longlong_as_double((long long)(((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]));
+    return a + b;
+}
+
+// Wave-wide sum, every lane receives it.  Fixed order: ror 8, 4, 2, 1 inside
+// each row of 16, then rows (0+1, 2+3), then halves.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_ror<8>(v);
+    v += dpp_ror<4>(v);
+    v += dpp_ror<2>(v);
+    v += dpp_ror<1>(v);
+    v = xor16_add(v);
+    return xor32_add(v);
+}
+
+// Inclusive prefix sum over the wave (row_shr 1, 2, 4, 8, then row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+    return x;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+    v = max(v, dpp_ror<8>(v));
+    v = max(v, dpp_ror<4>(v));
+    v = max(v, dpp_ror<2>(v));
+    v = max(v, dpp_ror<1>(v));
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = max((int)r[0], (int)r[1]);
+    }
+    {
+        auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = max((int)r[0], (int)r[1]);
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the block in thread order; `total` = block sum.
+// `lds` holds >= 16 ints.  Every thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    const int incl = wave_incl_scan(v);
+    if (lane == kWave - 1) lds[w] = incl;
+    lds_barrier();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int c = lds[i];
+        tot += c;
+        off += i < w ? c : 0;
+    }
+    lds_barrier();
+    total = tot;
+    return off + incl - v;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_max(int v, int* lds) {
+    constexpr int NW = NT / kWave;
+    v = wave_max(v);
+    if (lane_id() == 0) lds[threadIdx.x / kWave] = v;
+    lds_barrier();
+    int m = lds[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) m = max(m, lds[i]);
+    lds_barrier();
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// Keys with contiguous ownership: thread t holds elements t*P .. t*P + P - 1,
+// read with 16-byte loads.  `readable` (a multiple of the vector width) bounds
+// what may be read; elements at or beyond `n` are marked invalid.
+// ---------------------------------------------------------------------------
+template <int P>
+__device__ __forceinline__ void load_u32_contig(const uint32_t* __restrict__ src, int n, int readable,
+                                                uint32_t (&v)[P], bool (&valid)[P]) {
+    static_assert(P % 4 == 0, "16-byte loads");
+    const int base = (int)threadIdx.x * P;
+#pragma unroll
+    for (int q = 0; q < P; q += 4) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (base + q < readable) u = *reinterpret_cast<const uint4*>(src + base + q);
+        v[q] = u.x; v[q + 1] = u.y; v[q + 2] = u.z; v[q + 3] = u.w;
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) valid[q] = base + q < n;
+}
+
+template <int P>
+__device__ __forceinline__ void load_u16_contig(const uint16_t* __restrict__ src, int n, int readable,
+                                                uint32_t (&v)[P], bool (&valid)[P]) {
+    static_assert(P % 8 == 0, "16-byte loads");
+    const int base = (int)threadIdx.x * P;
+#pragma unroll
+    for (int q = 0; q < P; q += 8) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (base + q < readable) u = *reinterpret_cast<const uint4*>(src + base + q);
+        v[q] = u.x & 0xffffu; v[q + 1] = u.x >> 16;
+        v[q + 2] = u.y & 0xffffu; v[q + 3] = u.y >> 16;
+        v[q + 4] = u.z & 0xffffu; v[q + 5] = u.z >> 16;
+        v[q + 6] = u.w & 0xffffu; v[q + 7] = u.w >> 16;
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) valid[q] = base + q < n;
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide selection of the k largest of the valid keys (keys < 2^nbits),
+// ties to the lowest index (index of element (t, q) = t * P + q).
+//
+// 1) coarse: one radix digit of <= 11 bits in a window that starts at the
+//    highest bit set in any key, so the keys spread over as many bins as the
+//    data allow.  Keys whose digit is above the threshold bin are certainly
+//    kept ("certain"); keys in the threshold bin are "candidates", written to
+//    an LDS array.  A caller can start work on the certain keys here.
+// 2) refine: the remaining digits over the candidate array only.
+// 3) keep: exact flags and ranks in index order for every key.
+// LDS: `hist` >= 2049 uints, `sc` >= 24 ints, `cand` >= number of candidates
+// (at most the number of valid keys).  Every thread calls every step.
+// ---------------------------------------------------------------------------
+struct SelectState {
+    uint32_t prefix;   // resolved high bits of the k-th largest key
+    int shift;         // bits below the resolved ones
+    int above;         // keys whose resolved bits exceed the prefix (all > T)
+    int krem;          // k - above
+    int ncand;         // candidates (keys whose resolved bits equal the prefix)
+};
+
+// Scan `nb` bins in descending order and find the one holding the krem-th key.
+template <int NT>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int krem, int* sc,
+                                         uint32_t& digit, int& above) {
+    const int per = (nb + NT - 1) / NT;   // consecutive descending bins per thread
+    int mine = 0;
+    for (int q = 0; q < per; ++q) {
+        const int r = threadIdx.x * per + q;
+        if (r < nb) mine += (int)hist[nb - 1 - r];
+    }
+    int tot;
+    int cum = block_excl_scan<NT>(mine, sc, tot);
+    for (int q = 0; q < per; ++q) {
+        const int r = threadIdx.x * per + q;
+        if (r < nb) {
+            const int c = (int)hist[nb - 1 - r];
+            if (cum < krem && krem <= cum + c) {
+                sc[20] = nb - 1 - r;
+                sc[21] = cum;
+            }
+            cum += c;
+        }
+    }
+    lds_barrier();
+    digit = (uint32_t)sc[20];
+    above = sc[21];
+    lds_barrier();
+}
+
+// Coarse digit.  cert[q] / cand[q] classify each key; candidates go to `cand`
+// in index order (only when digits remain to be resolved).  `cert_rank` is the
+// index-order rank of this thread's first certain key; st.above = certain keys.
+// Requires 1 <= k <= number of valid keys.
+template <int P, int NT>
+__device__ SelectState block_select_coarse(const uint32_t (&key)[P], const bool (&valid)[P], int k,
+                                           int nbits, bool (&cert)[P], int& cert_rank,
+                                           uint32_t* hist, int* sc, uint32_t* cand) {
+    int kmax = 0;
+#pragma unroll
+    for (int q = 0; q < P; ++q) kmax = max(kmax, valid[q] ? (int)key[q] : 0);
+    kmax = block_max<NT>(kmax, sc);
+    int top = 32 - __clz(kmax);            // significant bits (0 when every key is 0)
+    if (top > nbits) top = nbits;
+    SelectState st{0u, top, 0, k, 0};       // bits at or above `top` are zero in every key
+    if (top > 0) {
+        const int dw = top >= 11 ? 11 : top;
+        const int nb = 1 << dw;
+        st.shift = top - dw;
+        for (int b = threadIdx.x; b <= nb; b += NT) hist[b] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < P; ++q) atomicAdd(&hist[valid[q] ? (key[q] >> st.shift) : (uint32_t)nb], 1u);
+        lds_barrier();
+        uint32_t digit;
+        find_bin<NT>(hist, nb, k, sc, digit, st.above);
+        st.prefix = digit;
+        st.krem = k - st.above;
+    }
+    int nc = 0, nd = 0;
+    bool cd[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const uint32_t hi = key[q] >> st.shift;
+        cert[q] = valid[q] && hi > st.prefix;
+        cd[q] = valid[q] && hi == st.prefix;
+        nc += cert[q] ? 1 : 0;
+        nd += cd[q] ? 1 : 0;
+    }
+    int tot;
+    const int pre = block_excl_scan<NT>((nc << 16) | nd, sc, tot);
+    cert_rank = pre >> 16;
+    st.ncand = tot & 0xffff;
+    if (st.shift > 0) {
+        int cp = pre & 0xffff;
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            if (cd[q]) cand[cp] = key[q];
+            cp += cd[q] ? 1 : 0;
+        }
+    }
+    lds_barrier();
+    return st;
+}
+
+// Remaining digits over the candidate array.  T = the k-th largest key,
+// cgt = number of keys > T.
+template <int NT>
+__device__ void block_select_refine(SelectState& st, const uint32_t* cand, uint32_t& T, int& cgt,
+                                    uint32_t* hist, int* sc) {
+    while (st.shift > 0) {
+        const int dw = st.shift >= 11 ? 11 : st.shift;
+        const int nb = 1 << dw;
+        const int shift = st.shift - dw;
+        for (int b = threadIdx.x; b < nb; b += NT) hist[b] = 0u;
+        lds_barrier();
+        for (int i = threadIdx.x; i < st.ncand; i += NT) {
+            const uint32_t v = cand[i];
+            if ((v >> st.shift) == st.prefix) atomicAdd(&hist[(v >> shift) & (nb - 1)], 1u);
+        }
+        lds_barrier();
+        uint32_t digit;
+        int ab;
+        find_bin<NT>(hist, nb, st.krem, sc, digit, ab);
+        st.above += ab;
+        st.krem -= ab;
+        st.prefix = (st.prefix << dw) | digit;
+        st.shift = shift;
+    }
+    T = st.prefix;
+    cgt = st.above;
+}
+
+// Keep exactly k of the valid keys: every key > T and the lowest-index keys
+// equal to T (all = keep every valid key).  pos[q] is the rank of a kept key
+// in ascending index order.  One block scan of the packed per-thread counts
+// (keys > T in the high half, keys == T in the low half: fewer than k <= 2^15
+// keys exceed T and at most 2^15 equal it, so the packed sum stays below 2^31).
+// Returns the number kept.  `sc` >= 16 ints of LDS.
+template <int P, int NT>
+__device__ int block_keep_and_rank(const uint32_t (&key)[P], const bool (&valid)[P], bool all,
+                                   int k, uint32_t T, int cgt, bool (&on)[P], int (&pos)[P],
+                                   int* sc) {
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        gt += (valid[q] && (all || key[q] > T)) ? 1 : 0;
+        eq += (valid[q] && !all && key[q] == T) ? 1 : 0;
+    }
+    int tot;
+    // keep-all counts may reach 2^15, so they are scanned unpacked
+    const int pre = block_excl_scan<NT>(all ? gt : ((gt << 16) | eq), sc, tot);
+    const int need = all ? 0 : k - cgt;
+    int eq_before = all ? 0 : (pre & 0xffff);
+    int kept = all ? pre : (pre >> 16) + min(eq_before, need);
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const bool e = valid[q] && !all && key[q] == T;
+        on[q] = valid[q] && k > 0 && (all || key[q] > T || (e && eq_before < need));
+        eq_before += e ? 1 : 0;
+        pos[q] = kept;
+        kept += on[q] ? 1 : 0;
+    }
+    return all ? tot : (tot >> 16) + min(tot & 0xffff, need);
+}
+
+}  // namespace prox

@@ -1,0 +1,63 @@
+// Host-side declarations shared by the Prox library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace prox {
+
+constexpr int kInt4Group = 128;
+constexpr int kTileRowBytes = 128;   // bytes of one tile row of the proxy (one cache line)
+constexpr int kMaxW2Total = 512;     // upper bound on Stage-2 blocks per launch (all tokens)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int tile_channels(int kind) { return kind == 1 ? 64 : 128; }
+inline int f_pad_of(int F, int kind) { return (int)align_up((size_t)F, (size_t)tile_channels(kind)); }
+
+struct ProxyView {
+    int kind;          // 1 int8, 2 int4
+    int d, F, f_pad, groups;
+    const uint8_t* codes;  // tile-major: [f_pad / tile_ch][d][128 B]
+    const float* scales;   // gate [groups][f_pad] then up [groups][f_pad]
+};
+
+// Stage-2 blocks per token: about one block per compute unit over the batch.
+inline int stage2_blocks_max(int batch) {
+    int w = kMaxW2Total / batch;
+    return w < 1 ? 1 : w;
+}
+inline int stage2_blocks(int batch, int k_ff, int n_cu) {
+    int w = n_cu / batch;
+    if (w > stage2_blocks_max(batch)) w = stage2_blocks_max(batch);
+    if (w > k_ff) w = k_ff;
+    return w < 1 ? 1 : w;
+}
+
+// Workspace carve-up (byte offsets) for one (d, F, B, kind).
+struct WsLayout {
+    size_t key, ypart, total;
+};
+inline WsLayout ws_layout(int d, int F, int B, int kind) {
+    const int fp = f_pad_of(F, kind);
+    WsLayout L;
+    size_t o = 0;
+    L.key = o;    o = align_up(o + (size_t)B * fp * 4, 256);
+    L.ypart = o;  o = align_up(o + (size_t)B * stage2_blocks_max(B) * d * 4, 256);
+    L.total = o;
+    return L;
+}
+
+// ---- launchers (prox_kernels.hip); all enqueue on `s` and return the launch status
+hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d, int F,
+                              const ProxyView& p, hipStream_t s);
+hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
+                         double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
+                         hipStream_t s);
+hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
+                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
+                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart,
+                         hipStream_t s);
+hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s);
+
+}  // namespace prox

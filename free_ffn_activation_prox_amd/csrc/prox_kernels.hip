@@ -1,0 +1,823 @@
+// Prox sparse SwiGLU FFN: gfx950 kernels.
+//
+// One forward = three launches (Prox, Abstract; SwiGLU as in PrunePath, §2.1, Eq. (1)):
+//   stage1   per (channel tile, token): input selection (top-k_in of |x|, redone in
+//            every block: x is a few KB), proxy GEMV over the kept rows of the tile,
+//            h~ = silu(g~) u~ in fp64 and the fp32 ranking key |h~|
+//   stage2   per (block, token): top-k of the keys (redone in every block: the keys
+//            are a few tens of KB), the block's slice of the ranked channel list,
+//            then for each of its channels the exact gate/up dots over the dense x,
+//            h = silu(g) u and h * W_down row into the block's partial y
+//   reduce   y = fixed-order sum of the block partials
+// plus the one-time proxy build.
+//
+// Proxy layout (tile-major): the codes of one channel tile (64 channels int8,
+// 128 channels int4) for input row i are one 128-byte line at
+// (tile * d + i) * 128, so a block streams only the kept rows of its tile and
+// every row it touches is exactly one cache line.
+#include "prox_device.hpp"
+#include "prox_internal.hpp"
+
+namespace prox {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ int sext8(uint32_t w, int c) { return (int)(w << (24 - 8 * c)) >> 24; }
+__device__ __forceinline__ int sext4(uint32_t w, int c) { return (int)(w << (28 - 4 * c)) >> 28; }
+
+// code = clamp(round-half-even(fp32(w / s)), -qmax, qmax); 0 when s == 0.
+// The quotient is formed in fp64 and rounded once to fp32: for fp32 operands an
+// fp64 quotient rounded to fp32 equals the correctly rounded fp32 quotient
+// (53 >= 2 * 24 + 2), independent of fast-division compiler settings.
+__device__ __forceinline__ int quant_code(float w, float s, float qmax) {
+    if (!(s > 0.f)) return 0;
+    float r = (float)((double)w / (double)s);
+    float q = rintf(r);
+    q = fminf(fmaxf(q, -qmax), qmax);
+    return (int)q;
+}
+
+// ---------------------------------------------------------------------------
+// Proxy build: scales.  grid (f_pad / 4, groups, 2), block 256: one wave per
+// (channel, group, matrix); max |w| over the group, s = fp32(max / qmax).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_quant_scales(const uint16_t* __restrict__ wg_t,
+                                                      const uint16_t* __restrict__ wu_t, int d,
+                                                      int F, int f_pad, int groups, float qmax,
+                                                      float* __restrict__ scales) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + wave;
+    const int g = blockIdx.y, mat = blockIdx.z;
+    if (j >= f_pad) return;
+    const uint16_t* w = mat == 0 ? wg_t : wu_t;
+    const int gs = d / groups;
+    float amax = 0.f;
+    if (j < F) {
+        const uint16_t* row = w + (size_t)j * d + (size_t)g * gs;
+        for (int i = lane; i < gs; i += kWave) amax = fmaxf(amax, fabsf(bf16_to_f32(row[i])));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    if (lane == 0) {
+        float s = (float)((double)amax / (double)qmax);
+        scales[((size_t)mat * groups + g) * f_pad + j] = (j < F) ? s : 0.f;
+    }
+}
+
+// Proxy build: codes.  grid (ceil(d / 256), f_pad / CB), block 256: thread = (input i,
+// block of CB channels: 8 for int8, 16 for int4); reads W^T[j][i] (coalesced over
+// i) and writes one 16-byte code block into the tile-major layout.
+template <int KIND>
+__global__ void __launch_bounds__(256) k_quant_codes(const uint16_t* __restrict__ wg_t,
+                                                     const uint16_t* __restrict__ wu_t, int d,
+                                                     int F, int f_pad, int groups,
+                                                     const float* __restrict__ scales,
+                                                     uint8_t* __restrict__ codes) {
+    constexpr int CB = KIND == 1 ? 8 : 16;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int cb = blockIdx.y;
+    if (i >= d) return;
+    const int g = i / (d / groups);
+    const float qmax = KIND == 1 ? 127.f : 7.f;
+    uint32_t pg[2] = {0, 0}, pu[2] = {0, 0};
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const int j = cb * CB + c;
+        float wgv = 0.f, wuv = 0.f;
+        if (j < F) {
+            wgv = bf16_to_f32(wg_t[(size_t)j * d + i]);
+            wuv = bf16_to_f32(wu_t[(size_t)j * d + i]);
+        }
+        const int qg = quant_code(wgv, scales[(size_t)g * f_pad + j], qmax);
+        const int qu = quant_code(wuv, scales[((size_t)groups + g) * f_pad + j], qmax);
+        if (KIND == 1) {
+            pg[c >> 2] |= (uint32_t)(qg & 0xff) << (8 * (c & 3));
+            pu[c >> 2] |= (uint32_t)(qu & 0xff) << (8 * (c & 3));
+        } else {
+            pg[c >> 3] |= (uint32_t)(qg & 0xf) << (4 * (c & 7));
+            pu[c >> 3] |= (uint32_t)(qu & 0xf) << (4 * (c & 7));
+        }
+    }
+    const int tile = cb / 8, lb = cb % 8;
+    uint4 v = make_uint4(pg[0], pg[1], pu[0], pu[1]);
+    *reinterpret_cast<uint4*>(codes + ((size_t)tile * d + i) * kTileRowBytes + lb * 16) = v;
+}
+
+hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d, int F,
+                              const ProxyView& p, hipStream_t s) {
+    float* scales = const_cast<float*>(p.scales);
+    const float qmax = p.kind == 1 ? 127.f : 7.f;
+    hipLaunchKernelGGL(k_quant_scales, dim3(p.f_pad / 4, p.groups, 2), dim3(256), 0, s, wg_t,
+                       wu_t, d, F, p.f_pad, p.groups, qmax, scales);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    uint8_t* codes = const_cast<uint8_t*>(p.codes);
+    if (p.kind == 1)
+        hipLaunchKernelGGL(k_quant_codes<1>, dim3((d + 255) / 256, p.f_pad / 8), dim3(256), 0, s,
+                           wg_t, wu_t, d, F, p.f_pad, p.groups, p.scales, codes);
+    else
+        hipLaunchKernelGGL(k_quant_codes<2>, dim3((d + 255) / 256, p.f_pad / 16), dim3(256), 0, s,
+                           wg_t, wu_t, d, F, p.f_pad, p.groups, p.scales, codes);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1.  grid (tiles, B), block 512 (8 waves).
+//
+// Input selection: thread t holds x[p * 512 + t] (p < PX); keys are the 15
+// magnitude bits of the bf16 value (monotone in |x|, -0 == +0).  The kept
+// inputs, ascending, go to LDS as (index << 16 | bf16 bits).
+//
+// GEMV: the kept list is cut into chunks of 8 consecutive entries; row slot s
+// (= 8 * wave + lane / 8, 64 slots) takes chunks s, s + 64, ...; lane % 8 picks
+// a 16-byte block of the tile row (int8: 8 gate + 8 up codes; int4: 16 + 16).
+// int8 chunks accumulate in fp32 when the chunk's x exponents span <= 6
+// binades: every product x * q is then a multiple of 2^(e_lo - 7) below
+// 2^(e_hi + 8), so the partial sums of <= 8 products are integers below 2^24 in
+// those units and every fp32 step is exact; the chunk sum is then added to the
+// fp64 accumulator.  Other chunks accumulate in fp64 directly.  int4
+// accumulates in fp64 and scales each 128-input group's inner sum when the
+// group changes.  The slots are reduced with lane shuffles and LDS in a fixed
+// order, so the result is deterministic.
+// ---------------------------------------------------------------------------
+struct Stage1Args {
+    const uint16_t* x;
+    int d, k_in;
+    ProxyView p;
+    float* key;          // [B][f_pad]
+    double* h_tap;       // [B][F] or null
+    float* key_tap;      // [B][F] or null
+    int32_t* in_idx_tap; // [B][k_in] or null
+};
+
+constexpr int kS1Threads = 512;
+constexpr int kSlots = 64;
+constexpr int kChunk = 8;
+
+// Certain-or-all classification shared by both stages: with `all`, every
+// valid key is certain; otherwise the coarse digit decides.
+template <int P, int NT>
+__device__ __forceinline__ SelectState classify(const uint32_t (&key)[P], const bool (&valid)[P],
+                                                int k, bool all, int nbits, bool (&cert)[P],
+                                                int& cert_rank, uint32_t* hist, int* sc,
+                                                uint32_t* cand) {
+    if (all || k == 0) {
+        int nc = 0;
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            cert[q] = all && valid[q];
+            nc += cert[q] ? 1 : 0;
+        }
+        int tot;
+        cert_rank = block_excl_scan<NT>(nc, sc, tot);
+        return SelectState{0u, 0, tot, k - tot, 0};
+    }
+    return block_select_coarse<P, NT>(key, valid, k, nbits, cert, cert_rank, hist, sc, cand);
+}
+
+// One chunk of <= 8 kept rows for one lane: the packed list entries and the
+// lane's 16-byte block of each tile row.
+struct Chunk {
+    uint32_t e[kChunk];
+    uint4 v[kChunk];
+};
+
+__device__ __forceinline__ void load_chunk(const uint32_t* list, int k_in, int ch, int nchunks,
+                                           const uint8_t* base, Chunk& c) {
+    const int r0 = ch * kChunk;
+    const int n = ch < nchunks ? min(kChunk, k_in - r0) : 0;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+        if (u < n) {
+            c.e[u] = list[r0 + u];
+            c.v[u] = *reinterpret_cast<const uint4*>(base + (size_t)(c.e[u] >> 16) * kTileRowBytes);
+        } else {
+            c.e[u] = 0;                       // x = +0: contributes nothing
+            c.v[u] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// Input selection of Stage 1.  The kept list holds (index << 16 | bf16 bits):
+// first the certain inputs in index order, then the kept candidates in index
+// order (the GEMV sums over the list, so only the set matters).  Then one
+// flag per chunk of 8 entries: 1 when the chunk's x exponents span at most
+// `spread_limit` binades (its products can be summed exactly in fp32).
+template <int PX>
+__device__ int stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32_t* cand,
+                             uint8_t* flags, uint32_t* hist, int* sc, int spread_limit) {
+    const int t = threadIdx.x;
+    const int k_in = a.k_in;
+    uint32_t raw[PX], key[PX];
+    bool valid[PX];
+    load_u16_contig<PX>(a.x + (size_t)b * a.d, a.d, a.d, raw, valid);
+#pragma unroll
+    for (int q = 0; q < PX; ++q) key[q] = raw[q] & 0x7fffu;
+    const bool all = k_in >= a.d;
+    bool cert[PX];
+    int crank;
+    SelectState st = classify<PX, kS1Threads>(key, valid, k_in, all, 15, cert, crank, hist, sc, cand);
+    const int cbase = crank;   // certain keys before this thread's elements
+#pragma unroll
+    for (int q = 0; q < PX; ++q) {
+        if (cert[q]) list[crank] = ((uint32_t)(t * PX + q) << 16) | raw[q];
+        crank += cert[q] ? 1 : 0;
+    }
+    // the candidates of the threshold bin (none when all or k_in == 0)
+    const int n_cert = st.above;
+    if (!all && k_in > 0) {
+        uint32_t T;
+        int cgt;
+        block_select_refine<kS1Threads>(st, cand, T, cgt, hist, sc);
+        bool on[PX];
+        int pos[PX];
+        block_keep_and_rank<PX, kS1Threads>(key, valid, false, k_in, T, cgt, on, pos, sc);
+        int cb = 0;     // certain keys of this thread before element q
+#pragma unroll
+        for (int q = 0; q < PX; ++q) {
+            const int j = t * PX + q;
+            if (on[q] && !cert[q]) list[n_cert + pos[q] - (cbase + cb)] = ((uint32_t)j << 16) | raw[q];
+            if (on[q] && a.in_idx_tap && blockIdx.x == 0) a.in_idx_tap[(size_t)b * k_in + pos[q]] = j;
+            cb += cert[q] ? 1 : 0;
+        }
+    } else if (all && a.in_idx_tap && blockIdx.x == 0) {
+#pragma unroll
+        for (int q = 0; q < PX; ++q)
+            if (cert[q]) a.in_idx_tap[(size_t)b * k_in + t * PX + q] = t * PX + q;
+    }
+    lds_barrier();
+    const int nchunks = (k_in + kChunk - 1) / kChunk;
+    for (int c = t; c < nchunks; c += kS1Threads) {
+        int lo = 255, hi = 0;
+        bool ok = true;
+        const int n = min(kChunk, k_in - c * kChunk);
+        for (int u = 0; u < n; ++u) {
+            const uint32_t r = list[c * kChunk + u];
+            const int e = (int)((r >> 7) & 0xffu);
+            if ((r & 0x7fffu) == 0) continue;   // +-0 contributes exactly 0
+            if (e == 0) ok = false;              // subnormal x: take the fp64 path
+            lo = min(lo, e);
+            hi = max(hi, e);
+        }
+        flags[c] = (ok && hi - lo <= spread_limit) ? 1 : 0;
+    }
+    lds_barrier();
+    return nchunks;
+}
+
+// int8 chunk: 8 gate + 8 up channels of the lane.
+__device__ __forceinline__ void consume_chunk_i8(const Chunk& c, bool exact32, double (&ag)[8],
+                                                 double (&au)[8]) {
+    if (exact32) {
+        float sg[8], su[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sg[q] = su[q] = 0.f;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float xf = bf16f(c.e[u] & 0xffffu);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sg[q] = fmaf(xf, (float)sext8(c.v[u].x, q), sg[q]);
+                sg[q + 4] = fmaf(xf, (float)sext8(c.v[u].y, q), sg[q + 4]);
+                su[q] = fmaf(xf, (float)sext8(c.v[u].z, q), su[q]);
+                su[q + 4] = fmaf(xf, (float)sext8(c.v[u].w, q), su[q + 4]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            ag[q] += (double)sg[q];
+            au[q] += (double)su[q];
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const double xd = (double)bf16f(c.e[u] & 0xffffu);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ag[q] = fma(xd, (double)sext8(c.v[u].x, q), ag[q]);
+                ag[q + 4] = fma(xd, (double)sext8(c.v[u].y, q), ag[q + 4]);
+                au[q] = fma(xd, (double)sext8(c.v[u].z, q), au[q]);
+                au[q + 4] = fma(xd, (double)sext8(c.v[u].w, q), au[q + 4]);
+            }
+        }
+    }
+}
+
+// int4 chunk: 16 gate + 16 up channels of the lane; the inner sums of a
+// 128-input group are scaled into og/ou when the row's group changes.
+__device__ __forceinline__ void consume_chunk_i4(const Chunk& c, int n, const float* sgp,
+                                                 const float* sup, int f_pad, int& cur,
+                                                 double (&ag)[16], double (&au)[16],
+                                                 double (&og)[16], double (&ou)[16]) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+        if (u < n) {
+            const int g = (int)(c.e[u] >> 16) >> 7;
+            if (g != cur) {
+                if (cur >= 0) {
+                    const float4* s4g = reinterpret_cast<const float4*>(sgp + (size_t)cur * f_pad);
+                    const float4* s4u = reinterpret_cast<const float4*>(sup + (size_t)cur * f_pad);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 fg = s4g[q], fu = s4u[q];
+                        og[4 * q + 0] = fma(ag[4 * q + 0], (double)fg.x, og[4 * q + 0]);
+                        og[4 * q + 1] = fma(ag[4 * q + 1], (double)fg.y, og[4 * q + 1]);
+                        og[4 * q + 2] = fma(ag[4 * q + 2], (double)fg.z, og[4 * q + 2]);
+                        og[4 * q + 3] = fma(ag[4 * q + 3], (double)fg.w, og[4 * q + 3]);
+                        ou[4 * q + 0] = fma(au[4 * q + 0], (double)fu.x, ou[4 * q + 0]);
+                        ou[4 * q + 1] = fma(au[4 * q + 1], (double)fu.y, ou[4 * q + 1]);
+                        ou[4 * q + 2] = fma(au[4 * q + 2], (double)fu.z, ou[4 * q + 2]);
+                        ou[4 * q + 3] = fma(au[4 * q + 3], (double)fu.w, ou[4 * q + 3]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) ag[q] = au[q] = 0.0;
+                }
+                cur = g;
+            }
+            const double xd = (double)bf16f(c.e[u] & 0xffffu);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                ag[q] = fma(xd, (double)sext4(c.v[u].x, q), ag[q]);
+                ag[q + 8] = fma(xd, (double)sext4(c.v[u].y, q), ag[q + 8]);
+                au[q] = fma(xd, (double)sext4(c.v[u].z, q), au[q]);
+                au[q + 8] = fma(xd, (double)sext4(c.v[u].w, q), au[q + 8]);
+            }
+        }
+    }
+}
+
+template <int KIND, int PX>
+__global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) {
+    constexpr int TC = KIND == 1 ? 64 : 128;            // channels per tile
+    constexpr int NV = KIND == 1 ? 8 : 16;               // channels per lane
+    extern __shared__ uint32_t dyn[];
+    __shared__ uint32_t hist[2048 + 64];
+    __shared__ int sc[24];
+    __shared__ double red[8][2][TC];
+
+    const int b = blockIdx.y;
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int k_in = a.k_in, d = a.d;
+    uint32_t* list = dyn;                         // [k_in]
+    uint32_t* cand = dyn + k_in;                  // [d]
+    uint8_t* flags = reinterpret_cast<uint8_t*>(dyn + k_in + d);
+    const int nchunks = stage1_select<PX>(a, b, list, cand, flags, hist, sc, 6);
+
+    const int slot = w * 8 + (l >> 3);
+    const int cb = l & 7;
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        const uint8_t* base = a.p.codes + (size_t)tile * d * kTileRowBytes + cb * 16;
+        double ag[NV], au[NV];
+#pragma unroll
+        for (int c = 0; c < NV; ++c) ag[c] = au[c] = 0.0;
+
+        // chunks slot, slot + 64, ...: the next chunk's rows are in flight while
+        // the current one is accumulated
+        Chunk c0, c1;
+        if constexpr (KIND == 1) {
+            load_chunk(list, k_in, slot, nchunks, base, c0);
+            for (int ch = slot; ch < nchunks; ch += 2 * kSlots) {
+                load_chunk(list, k_in, ch + kSlots, nchunks, base, c1);
+                consume_chunk_i8(c0, flags[ch] != 0, ag, au);
+                if (ch + kSlots >= nchunks) break;
+                load_chunk(list, k_in, ch + 2 * kSlots, nchunks, base, c0);
+                consume_chunk_i8(c1, flags[ch + kSlots] != 0, ag, au);
+            }
+        } else {
+            const float* sgp = a.p.scales + (size_t)tile * TC + cb * 16;
+            const float* sup = sgp + (size_t)a.p.groups * a.p.f_pad;
+            double og[NV], ou[NV];
+#pragma unroll
+            for (int c = 0; c < NV; ++c) og[c] = ou[c] = 0.0;
+            int cur = -1;
+            load_chunk(list, k_in, slot, nchunks, base, c0);
+            for (int ch = slot; ch < nchunks; ch += 2 * kSlots) {
+                load_chunk(list, k_in, ch + kSlots, nchunks, base, c1);
+                consume_chunk_i4(c0, min(kChunk, k_in - ch * kChunk), sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
+                if (ch + kSlots >= nchunks) break;
+                load_chunk(list, k_in, ch + 2 * kSlots, nchunks, base, c0);
+                consume_chunk_i4(c1, min(kChunk, k_in - (ch + kSlots) * kChunk), sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
+            }
+            if (cur >= 0) {
+                const float* sg = sgp + (size_t)cur * a.p.f_pad;
+                const float* su = sup + (size_t)cur * a.p.f_pad;
+#pragma unroll
+                for (int c = 0; c < NV; ++c) {
+                    og[c] = fma(ag[c], (double)sg[c], og[c]);
+                    ou[c] = fma(au[c], (double)su[c], ou[c]);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                ag[c] = og[c];
+                au[c] = ou[c];
+            }
+        }
+        // reduce the 8 row slots of the wave (lanes l ^ 8, l ^ 16, l ^ 32 share the
+        // channel block), then the 8 waves, in a fixed order
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+            ag[c] += dpp_ror8(ag[c]);
+            au[c] += dpp_ror8(au[c]);
+            ag[c] = xor32_add(xor16_add(ag[c]));
+            au[c] = xor32_add(xor16_add(au[c]));
+        }
+        if (l < 8) {
+#pragma unroll
+            for (int c = 0; c < NV; ++c) {
+                red[w][0][cb * NV + c] = ag[c];
+                red[w][1][cb * NV + c] = au[c];
+            }
+        }
+        lds_barrier();
+        if (t < TC) {
+            const int j = tile * TC + t;
+            if (j < a.p.F) {
+                double g = 0.0, u = 0.0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    g += red[q][0][t];
+                    u += red[q][1][t];
+                }
+                if (KIND == 1) {
+                    g *= (double)a.p.scales[j];
+                    u *= (double)a.p.scales[(size_t)a.p.f_pad + j];
+                }
+                const double h = g / (1.0 + exp(-g)) * u;
+                const float kf = (float)fabs(h);
+                a.key[(size_t)b * a.p.f_pad + j] = kf;
+                if (a.h_tap) a.h_tap[(size_t)b * a.p.F + j] = h;
+                if (a.key_tap) a.key_tap[(size_t)b * a.p.F + j] = kf;
+            }
+        }
+        lds_barrier();   // `red` is rewritten by the next tile
+    }
+}
+
+template <int KIND, int PX>
+static hipError_t go_stage1(const Stage1Args& a, int B, int n_cu, hipStream_t s) {
+    const int tiles = a.p.f_pad / (KIND == 1 ? 64 : 128);
+    const size_t dyn = (size_t)(a.k_in + a.d) * 4 + (a.k_in + kChunk - 1) / kChunk + 16;
+    auto fn = k_stage1<KIND, PX>;
+    if (dyn > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    // one block per compute unit over the batch; each block loops over tiles
+    int gx = n_cu / B;
+    if (gx < 1) gx = 1;
+    if (gx > tiles) gx = tiles;
+    hipLaunchKernelGGL(fn, dim3(gx, B), dim3(kS1Threads), dyn, s, a, tiles);
+    return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t stage1_px(const Stage1Args& a, int B, int n_cu, hipStream_t s) {
+    const int per = (a.d + kS1Threads - 1) / kS1Threads;
+    if (per <= 8) return go_stage1<KIND, 8>(a, B, n_cu, s);
+    if (per <= 16) return go_stage1<KIND, 16>(a, B, n_cu, s);
+    if (per <= 24) return go_stage1<KIND, 24>(a, B, n_cu, s);
+    return go_stage1<KIND, 32>(a, B, n_cu, s);
+}
+
+hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
+                         double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
+                         hipStream_t s) {
+    Stage1Args a{x, d, k_in, p, key, h_tap, key_tap, in_idx_tap};
+    return p.kind == 1 ? stage1_px<1>(a, B, n_cu, s) : stage1_px<2>(a, B, n_cu, s);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2.  grid (W2, B), block 512 (8 waves).
+//
+// Top-k: thread t holds key[p * 512 + t] (p < PK); fp32 keys of non-negative
+// values order like their bit patterns (31 bits).  Every block finds the same
+// kept set and the rank of each kept channel in ascending index order; block w
+// keeps ranks [w*k/W2, (w+1)*k/W2) in LDS, writes those entries of idx and the
+// mask bytes of channels [w*F/W2, (w+1)*F/W2).
+//
+// Sparse SwiGLU: thread t covers columns r*4096 + 8t .. +8 (r < R) of every
+// row.  Channels go G at a time, double-buffered: the gate/up/down rows of the
+// next group are in flight while the current group's gate/up dots (fp32) are
+// reduced across the block, h = silu(g) u is formed and h * W_down row is
+// accumulated into the thread's part of the block's partial y.
+// ---------------------------------------------------------------------------
+struct Stage2Args {
+    const uint16_t* x;
+    const uint16_t* wg_t;
+    const uint16_t* wu_t;
+    const uint16_t* wd;
+    const float* key;     // [B][f_pad]
+    int d, F, f_pad, k, W2;
+    int32_t* idx;         // [B][k] or null
+    uint8_t* mask;        // [B][F] or null
+    float* ypart;         // [B][W2][d]
+};
+
+constexpr int kS2Threads = 1024;
+
+// Column ownership inside a team of TEAM threads: thread tt covers columns
+// r * TEAM * 8 + tt * 8 .. +8 for r < R.
+template <int R, int G>
+struct RowGroup {
+    uint4 g[G][R], u[G][R], dn[G][R];
+};
+
+template <int R, int G, int TEAM>
+__device__ __forceinline__ void load_group(const Stage2Args& a, const int* chan, int n, int v0,
+                                           int team, int tt, RowGroup<R, G>& rg) {
+    constexpr int NTEAM = kS2Threads / TEAM;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int v = team + (v0 + q) * NTEAM;     // teams take list entries in turn
+        const bool ok = v < n;
+        const int j = ok ? chan[v] : 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int col = r * TEAM * 8 + tt * 8;
+            if (ok && col < a.d) {
+                const size_t off = (size_t)j * a.d + col;
+                rg.g[q][r] = *reinterpret_cast<const uint4*>(a.wg_t + off);
+                rg.u[q][r] = *reinterpret_cast<const uint4*>(a.wu_t + off);
+                rg.dn[q][r] = *reinterpret_cast<const uint4*>(a.wd + off);
+            } else {
+                rg.g[q][r] = rg.u[q][r] = rg.dn[q][r] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float dot8(const float (&x)[8], uint4 v, float acc) {
+    acc = fmaf(x[0], bf16_lo(v.x), acc); acc = fmaf(x[1], bf16_hi(v.x), acc);
+    acc = fmaf(x[2], bf16_lo(v.y), acc); acc = fmaf(x[3], bf16_hi(v.y), acc);
+    acc = fmaf(x[4], bf16_lo(v.z), acc); acc = fmaf(x[5], bf16_hi(v.z), acc);
+    acc = fmaf(x[6], bf16_lo(v.w), acc); acc = fmaf(x[7], bf16_hi(v.w), acc);
+    return acc;
+}
+
+__device__ __forceinline__ void axpy8(float h, uint4 v, float (&y)[8]) {
+    y[0] = fmaf(h, bf16_lo(v.x), y[0]); y[1] = fmaf(h, bf16_hi(v.x), y[1]);
+    y[2] = fmaf(h, bf16_lo(v.y), y[2]); y[3] = fmaf(h, bf16_hi(v.y), y[3]);
+    y[4] = fmaf(h, bf16_lo(v.z), y[4]); y[5] = fmaf(h, bf16_hi(v.z), y[5]);
+    y[6] = fmaf(h, bf16_lo(v.w), y[6]); y[7] = fmaf(h, bf16_hi(v.w), y[7]);
+}
+
+// Gate/up dots of a group (fp32), reduced over the team's waves through LDS
+// (`red` = this parity's [team][wave][2G] buffer), then h = silu(g) u and the
+// W_down rows accumulated into the thread's part of y.
+template <int R, int G, int TEAM>
+__device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const float (&xr)[R][8],
+                                              float (&yacc)[R][8], int n, int v0, float* red) {
+    constexpr int NTEAM = kS2Threads / TEAM;
+    constexpr int WPT = TEAM / kWave;      // waves per team
+    const int t = threadIdx.x, team = t / TEAM, tw = (t % TEAM) / kWave, l = t & 63;
+    float pg[G], pu[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        float ga = 0.f, ua = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ga = dot8(xr[r], rg.g[q][r], ga);
+            ua = dot8(xr[r], rg.u[q][r], ua);
+        }
+        pg[q] = wave_sum(ga);
+        pu[q] = wave_sum(ua);
+    }
+    float* my = red + (team * WPT) * (2 * G);
+    if (l == 0) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            my[tw * 2 * G + 2 * q] = pg[q];
+            my[tw * 2 * G + 2 * q + 1] = pu[q];
+        }
+    }
+    lds_barrier();
+    float h[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int v = 0; v < WPT; ++v) {
+            gs += my[v * 2 * G + 2 * q];
+            us += my[v * 2 * G + 2 * q + 1];
+        }
+        h[q] = (team + (v0 + q) * NTEAM < n) ? gs / (1.f + expf(-gs)) * us : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r) axpy8(h[q], rg.dn[q][r], yacc[r]);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2.  grid (W2, B), block 1024 (16 waves), split into 1024 / TEAM teams
+// of TEAM threads; each team covers a whole row (R chunks of TEAM * 8 columns).
+//
+// Top-k: thread t owns channels t*PK .. t*PK + PK - 1 (keys staged through
+// LDS).  After the first radix digit, channels above the threshold bin are
+// certainly kept: block w takes its share of them (by rank in index order) and
+// issues their row loads at once; the candidates of the threshold bin are then
+// resolved (remaining digits, lowest index first among equal keys) while those
+// loads are in flight, and the block appends its share of the kept candidates.
+// Every block computes the same kept set, so the shares partition it.  Block w
+// also writes the idx entries of ranks [w*k/W2, (w+1)*k/W2) and the mask bytes
+// of channels [w*F/W2, (w+1)*F/W2).
+//
+// Sparse SwiGLU: the teams take the block's channel list in turn; each walks
+// its part G channels at a time with the next group's gate/up/down rows in
+// flight.  Finally the teams' partial y are added and written as the block's
+// partial.
+// ---------------------------------------------------------------------------
+template <int PK, int R, int TEAM, int G>
+__global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
+    constexpr int NW = kS2Threads / kWave;
+    constexpr int NTEAM = kS2Threads / TEAM;
+    extern __shared__ uint32_t dyn2[];
+    __shared__ uint32_t hist[2048 + 64];
+    __shared__ int sc[24];
+    __shared__ float red[2][NW * 2 * G];
+
+    const int w = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int team = t / TEAM, tt = t % TEAM;
+    const int F = a.F, k = a.k, W2 = a.W2;
+    int* chan = reinterpret_cast<int*>(dyn2);            // [k / W2 + 2]
+    uint32_t* cand = dyn2 + (k + W2 - 1) / W2 + 2;       // [F]
+    // ---- x (this thread's columns) and the channel keys
+    float xr[R][8], yacc[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int col = r * TEAM * 8 + tt * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col < a.d) v = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
+        xr[r][0] = bf16_lo(v.x); xr[r][1] = bf16_hi(v.x);
+        xr[r][2] = bf16_lo(v.y); xr[r][3] = bf16_hi(v.y);
+        xr[r][4] = bf16_lo(v.z); xr[r][5] = bf16_hi(v.z);
+        xr[r][6] = bf16_lo(v.w); xr[r][7] = bf16_hi(v.w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
+    }
+    uint32_t kb[PK];
+    bool valid[PK];
+    load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(a.key + (size_t)b * a.f_pad), F, a.f_pad, kb, valid);
+    const bool all = k >= F;
+
+    // ---- certainly kept channels: this block's share, loads issued at once
+    bool cert[PK];
+    int crank;
+    SelectState st = classify<PK, kS2Threads>(kb, valid, k, all, 31, cert, crank, hist, sc, cand);
+    const int c_all = st.above;
+    const int c0 = (int)((long long)w * c_all / W2), c1 = (int)((long long)(w + 1) * c_all / W2);
+    const int cbase = crank;
+#pragma unroll
+    for (int q = 0; q < PK; ++q) {
+        if (cert[q] && crank >= c0 && crank < c1) chan[crank - c0] = t * PK + q;
+        crank += cert[q] ? 1 : 0;
+    }
+    const int nc = c1 - c0;
+    lds_barrier();
+    RowGroup<R, G> cur, nxt;
+    const bool early = nc >= G * NTEAM;           // the first group lies in the certain part
+    if (early) load_group<R, G, TEAM>(a, chan, nc, 0, team, tt, cur);
+
+    // ---- resolve the candidates while those loads are in flight
+    uint32_t T = 0;
+    int cgt = 0;
+    if (!all && k > 0) block_select_refine<kS2Threads>(st, cand, T, cgt, hist, sc);
+    bool on[PK];
+    int pos[PK];
+    block_keep_and_rank<PK, kS2Threads>(kb, valid, all, k, T, cgt, on, pos, sc);
+    // kept candidates: rank among them = rank among all kept - certain keys before
+    const int s_all = k - c_all;
+    const int s0 = (int)((long long)w * s_all / W2), s1 = (int)((long long)(w + 1) * s_all / W2);
+    const int r0 = (int)((long long)w * k / W2), r1 = (int)((long long)(w + 1) * k / W2);
+    const int m0 = (int)((long long)w * F / W2), m1 = (int)((long long)(w + 1) * F / W2);
+    int cb = cbase;
+#pragma unroll
+    for (int q = 0; q < PK; ++q) {
+        const int j = t * PK + q;
+        if (on[q] && !cert[q]) {
+            const int sr = pos[q] - cb;
+            if (sr >= s0 && sr < s1) chan[nc + sr - s0] = j;
+        }
+        cb += cert[q] ? 1 : 0;
+        if (a.idx && on[q] && pos[q] >= r0 && pos[q] < r1) a.idx[(size_t)b * k + pos[q]] = j;
+        if (a.mask && valid[q] && j >= m0 && j < m1) a.mask[(size_t)b * F + j] = on[q] ? 1 : 0;
+    }
+    const int n = nc + (s1 - s0);
+    lds_barrier();
+
+    // ---- sparse SwiGLU over the block's channels, two groups in flight
+    const int per_team = (n + NTEAM - 1) / NTEAM;
+    const int groups = (per_team + G - 1) / G;     // same trip count in every team
+    if (!early) load_group<R, G, TEAM>(a, chan, n, 0, team, tt, cur);
+    for (int gi = 0; gi < groups; gi += 2) {
+        load_group<R, G, TEAM>(a, chan, n, (gi + 1) * G, team, tt, nxt);
+        consume_group<R, G, TEAM>(cur, xr, yacc, n, gi * G, red[0]);
+        if (gi + 1 >= groups) break;
+        load_group<R, G, TEAM>(a, chan, n, (gi + 2) * G, team, tt, cur);
+        consume_group<R, G, TEAM>(nxt, xr, yacc, n, (gi + 1) * G, red[1]);
+    }
+    // ---- add the teams' partial y (teams > 0 go through LDS) and write
+    if constexpr (NTEAM > 1) {
+        lds_barrier();                                  // the channel list is dead
+        float* ybuf = reinterpret_cast<float*>(dyn2);   // [NTEAM - 1][TEAM][R * 8]
+        if (team > 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ybuf[((team - 1) * TEAM + tt) * R * 8 + r * 8 + e] = yacc[r][e];
+        }
+        lds_barrier();
+        if (team == 0) {
+            for (int m = 1; m < NTEAM; ++m)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) yacc[r][e] += ybuf[((m - 1) * TEAM + tt) * R * 8 + r * 8 + e];
+        }
+    }
+    if (team == 0) {
+        float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int col = r * TEAM * 8 + tt * 8;
+            if (col < a.d) {
+                *reinterpret_cast<float4*>(dst + col) = make_float4(yacc[r][0], yacc[r][1], yacc[r][2], yacc[r][3]);
+                *reinterpret_cast<float4*>(dst + col + 4) = make_float4(yacc[r][4], yacc[r][5], yacc[r][6], yacc[r][7]);
+            }
+        }
+    }
+}
+
+template <int PK, int R, int TEAM, int G>
+static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
+    constexpr int NTEAM = kS2Threads / TEAM;
+    const size_t lists = ((size_t)(a.k + a.W2 - 1) / a.W2 + 2 + (size_t)a.F) * 4;
+    const size_t ybuf = NTEAM > 1 ? (size_t)(NTEAM - 1) * TEAM * R * 8 * 4 : 0;
+    const size_t dyn = lists > ybuf ? lists : ybuf;
+    auto fn = k_stage2<PK, R, TEAM, G>;
+    if (dyn > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(a.W2, B), dim3(kS2Threads), dyn, s, a);
+    return hipGetLastError();
+}
+
+template <int R, int TEAM, int G>
+static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
+    const int per = (a.F + kS2Threads - 1) / kS2Threads;
+    if (per <= 4) return go_stage2<4, R, TEAM, G>(a, B, s);
+    if (per <= 8) return go_stage2<8, R, TEAM, G>(a, B, s);
+    if (per <= 12) return go_stage2<12, R, TEAM, G>(a, B, s);
+    if (per <= 16) return go_stage2<16, R, TEAM, G>(a, B, s);
+    if (per <= 20) return go_stage2<20, R, TEAM, G>(a, B, s);
+    if (per <= 24) return go_stage2<24, R, TEAM, G>(a, B, s);
+    if (per <= 28) return go_stage2<28, R, TEAM, G>(a, B, s);
+    return go_stage2<32, R, TEAM, G>(a, B, s);
+}
+
+hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
+                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
+                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart,
+                         hipStream_t s) {
+    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart};
+    if (d <= 4096) return stage2_pk<1, 512, 2>(a, B, s);
+    if (d <= 8192) return stage2_pk<1, 1024, 2>(a, B, s);
+    return stage2_pk<2, 1024, 1>(a, B, s);
+}
+
+// ---------------------------------------------------------------------------
+// y = sum of the W2 block partials, fixed order.  grid (ceil(d / 64), B),
+// block 256: lane = column, wave q sums partials q, q+4, ... into 8 running
+// sums (independent loads in flight), then the waves combine in LDS.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypart, int d, int W2,
+                                                  float* __restrict__ y) {
+    __shared__ float acc[4][64];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int col = blockIdx.x * 64 + lane;
+    float s[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s[u] = 0.f;
+    if (col < d) {
+        const float* src = ypart + (size_t)b * W2 * d + col;
+        int wv = q;
+        for (; wv + 28 < W2; wv += 32) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s[u] += src[(size_t)(wv + 4 * u) * d];
+        }
+        for (int u = 0; wv < W2; wv += 4, ++u) s[u & 7] += src[(size_t)wv * d];
+    }
+    float tot = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+    acc[q][lane] = tot;
+    __syncthreads();
+    if (q == 0 && col < d) y[(size_t)b * d + col] = (acc[0][lane] + acc[1][lane]) + (acc[2][lane] + acc[3][lane]);
+}
+
+hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s) {
+    hipLaunchKernelGGL(k_reduce_y, dim3((d + 63) / 64, B), dim3(256), 0, s, ypart, d, W2, y);
+    return hipGetLastError();
+}
+
+}  // namespace prox

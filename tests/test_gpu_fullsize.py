@@ -1,0 +1,99 @@
+"""GPU parity at the full sizes of the measured workloads, in the launch
+configuration the bench times (same entry point, same planner).
+
+B = 1 tokens are compared in full; for the batched workloads a sample of
+tokens (first, middle, last) is compared in full, the rest through the
+batch-row property (row b of a batched call equals the single-token call).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from prox_workloads import gen_weights, gen_x, workloads
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+_cache = {}
+
+
+def _layer(cfg_id, layer, d, F, kind):
+    from _gpu_common import Case
+    key = (cfg_id, layer)
+    if key not in _cache:
+        _cache.clear()
+        w = gen_weights(cfg_id, layer, d, F)
+        xb = np.zeros((1, d), dtype=np.uint16)
+        _cache[key] = Case(xb, w["wg_t"], w["wu_t"], w["wd"], kind)
+    return _cache[key]
+
+
+def _with_x(case, x_bits):
+    from _gpu_common import to_dev
+    from oracle import prox_oracle as O
+    case.xb = x_bits
+    case.x = O.bf16_bits_to_f64(x_bits)
+    case.B = x_bits.shape[0]
+    case.dx = to_dev(x_bits)
+    return case
+
+
+def _run(name, layer=0, tokens=None):
+    wl = workloads()[name]
+    shp = wl.layers[layer]
+    c = _layer(wl.config_id, layer, shp.d, shp.F, wl.proxy)
+    c.check_proxy()
+    _with_x(c, gen_x(wl, layer))
+    st = c.check(wl.k_in(layer), wl.k_ff(layer), tokens=tokens, label=f"{name} L{layer}")
+    print(f"[fullsize] {name} L{layer}: {st}", flush=True)
+    return c, wl
+
+
+@pytest.mark.parametrize("name", ["c2_s50", "c2_s70", "c2_s90"])
+def test_c2_llama7b_layer(name):
+    _run(name)
+
+
+@pytest.mark.parametrize("name", ["c4_b1_s50", "c4_b1_s70"])
+def test_c4_70b_layer(name):
+    _run(name)
+
+
+def test_c4_70b_batch8():
+    c, wl = _run("c4_b8_s70", tokens=[0, 3, 7])
+    _batch_rows(c, wl, 0)
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+@pytest.mark.parametrize("name", ["c3_b1", "c3_b4", "c3_b16"])
+def test_c3_llama3_8b_stack(name, layer):
+    wl = workloads()[name]
+    toks = None if wl.batch <= 4 else [0, wl.batch // 2, wl.batch - 1]
+    c, wl = _run(name, layer, tokens=toks)
+    if wl.batch > 4:
+        _batch_rows(c, wl, layer)
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_c5_mixed_stack(layer):
+    c, wl = _run("c5", layer, tokens=[0, 13, 31])
+    _batch_rows(c, wl, layer)
+
+
+def _batch_rows(c, wl, layer):
+    import free_ffn_activation_prox_amd as P
+    k_in, k_ff = wl.k_in(layer), wl.k_ff(layer)
+    yb, mb, _ = P.ffn_forward(c.dx, c.weights, c.proxy, k_in, k_ff)
+    for b in range(c.B):
+        y1, m1, _ = P.ffn_forward(c.dx[b:b + 1].contiguous(), c.weights, c.proxy, k_in, k_ff)
+        assert torch.equal(m1[0], mb[b]), f"token {b}: batched mask differs from single"
+        d = (y1[0] - yb[b]).abs().max().item()
+        s = y1[0].abs().max().item()
+        assert d <= 1e-5 * max(s, 1e-30), f"token {b}: batched y differs from single ({d} vs {s})"
