@@ -169,6 +169,7 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     float* key = reinterpret_cast<float*>(ws + L.key);
     float* ypart = reinterpret_cast<float*>(ws + L.ypart);
+    uint32_t* gh = reinterpret_cast<uint32_t*>(ws + L.gh);
     const int n_cu = device_cus();
     const int W2 = stage2_blocks(batch, k_ff, n_cu);
 
@@ -179,16 +180,16 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
 
     hipError_t e = mark(0);
     if (e != hipSuccess) return hip_fail(e, "event record");
-    e = launch_stage1(xb, batch, d, k_in, pv, key, taps ? taps->h_hat : nullptr,
+    e = launch_stage1(xb, batch, d, k_in, pv, key, gh, taps ? taps->h_hat : nullptr,
                       taps ? taps->key : nullptr, taps ? taps->in_idx : nullptr, n_cu, s);
     if (e != hipSuccess) return hip_fail(e, "stage 1");
     if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_stage2(xb, static_cast<const uint16_t*>(w->w_gate_t),
                       static_cast<const uint16_t*>(w->w_up_t), static_cast<const uint16_t*>(w->w_down),
-                      key, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart, s);
+                      key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart, s);
     if (e != hipSuccess) return hip_fail(e, "stage 2");
     if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
-    e = launch_reduce_y(ypart, batch, d, W2, y, s);
+    e = launch_reduce_y(ypart, batch, d, W2, y, gh, s);
     if (e != hipSuccess) return hip_fail(e, "reduce y");
     if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;

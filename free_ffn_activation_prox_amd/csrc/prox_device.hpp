@@ -23,6 +23,20 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ---- buffer loads: a scalar resource (base, byte size) + per-lane byte offset
+// + scalar byte offset.  The hardware returns zeros past the size.  Rows that
+// are uniform over a block then cost no per-lane address arithmetic.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -195,7 +209,7 @@ __device__ __forceinline__ void load_u16_contig(const uint16_t* __restrict__ src
 // 2) refine: the remaining digits over the candidate array only.
 // 3) keep: exact flags and ranks in index order for every key.
 // LDS: `hist` >= 2049 uints, `sc` >= 24 ints, `cand` >= number of candidates
-// (at most the number of valid keys).  Every thread calls every step.
+// (at most the number of valid keys) + 64.  Every thread calls every step.
 // ---------------------------------------------------------------------------
 struct SelectState {
     uint32_t prefix;   // resolved high bits of the k-th largest key
@@ -234,14 +248,93 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int krem,
     lds_barrier();
 }
 
-// Coarse digit.  cert[q] / cand[q] classify each key; candidates go to `cand`
-// in index order (only when digits remain to be resolved).  `cert_rank` is the
-// index-order rank of this thread's first certain key; st.above = certain keys.
-// Requires 1 <= k <= number of valid keys.
+// With the resolved digit (st.prefix at st.shift) known: cert[q] = key above
+// the threshold bin, candidates (digit == prefix) go to `cand` in index order
+// when bits remain below the digit.  Sets cert_rank (index-order rank of this
+// thread's first certain key) and st.ncand.
 template <int P, int NT>
-__device__ SelectState block_select_coarse(const uint32_t (&key)[P], const bool (&valid)[P], int k,
-                                           int nbits, bool (&cert)[P], int& cert_rank,
-                                           uint32_t* hist, int* sc, uint32_t* cand) {
+__device__ __forceinline__ void classify_prefix(const uint32_t (&key)[P], const bool (&valid)[P],
+                                                SelectState& st, bool (&cert)[P], int& cert_rank,
+                                                int* sc, uint32_t* cand) {
+    int nc = 0, nd = 0;
+    bool cd[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const uint32_t hi = key[q] >> st.shift;
+        cert[q] = valid[q] && hi > st.prefix;
+        cd[q] = valid[q] && hi == st.prefix;
+        nc += cert[q] ? 1 : 0;
+        nd += cd[q] ? 1 : 0;
+    }
+    int tot;
+    const int pre = block_excl_scan<NT>((nc << 16) | nd, sc, tot);
+    cert_rank = pre >> 16;
+    st.ncand = tot & 0xffff;
+    if (st.shift > 0) {
+        // branch-free: lanes without a candidate write a per-lane dummy word
+        int cp = pre & 0xffff;
+        uint32_t* dummy = cand + st.ncand + (threadIdx.x & 63);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            *(cd[q] ? cand + cp : dummy) = key[q];
+            cp += cd[q] ? 1 : 0;
+        }
+    }
+    lds_barrier();
+}
+
+// The coarse digit from a histogram built outside the block: NB bins of
+// key >> shift over the n valid keys, in global memory.  On success st holds
+// the threshold bin (prefix), `above` = keys in higher bins and krem = k -
+// above.  Returns false when the bins do not add up to n, i.e. the histogram
+// is not the one of these keys; the caller then ranks without it.
+// Requires 1 <= k <= n.
+template <int NT, int NB>
+__device__ bool block_hist_bin(const uint32_t* __restrict__ gh, int k, int n, int shift, int* sc,
+                               SelectState& st) {
+    constexpr int PER = NB / NT;   // bins per thread, descending from the top
+    static_assert(PER % 4 == 0 && PER * NT == NB, "16-byte loads of whole bins");
+    const uint4* src = reinterpret_cast<const uint4*>(gh + NB - ((int)threadIdx.x + 1) * PER);
+    uint32_t c[PER];   // c[i] = bin NB - (t + 1) * PER + i
+#pragma unroll
+    for (int v = 0; v < PER / 4; ++v) {
+        const uint4 u = src[v];
+        c[4 * v] = u.x; c[4 * v + 1] = u.y; c[4 * v + 2] = u.z; c[4 * v + 3] = u.w;
+    }
+    // A stale histogram may hold anything.  Bins are checked one by one, so a
+    // thread's contribution is its true sum (no wrap) or n + 1; the block
+    // total is n exactly when no bin is out of range and the bins add up.
+    uint32_t mine = 0;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        bad |= c[i] > (uint32_t)n;
+        mine += c[i];
+    }
+    int tot;
+    int cum = block_excl_scan<NT>(bad ? n + 1 : (int)min(mine, (uint32_t)n + 1u), sc, tot);
+    if (tot != n) return false;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+        const int cnt = (int)c[i];
+        if (cum < k && k <= cum + cnt) {
+            sc[20] = NB - ((int)threadIdx.x + 1) * PER + i;
+            sc[21] = cum;
+        }
+        cum += cnt;
+    }
+    lds_barrier();
+    st = SelectState{(uint32_t)sc[20], shift, sc[21], k - sc[21], 0};
+    lds_barrier();
+    return true;
+}
+
+// The coarse digit from the block's own keys: one radix digit of <= 11 bits
+// in a window that starts at the highest bit set in any key (keys < 2^nbits).
+// Same outputs as block_hist_bin.  Requires 1 <= k <= number of valid keys.
+template <int P, int NT>
+__device__ SelectState block_coarse_bin(const uint32_t (&key)[P], const bool (&valid)[P], int k,
+                                        int nbits, uint32_t* hist, int* sc) {
     int kmax = 0;
 #pragma unroll
     for (int q = 0; q < P; ++q) kmax = max(kmax, valid[q] ? (int)key[q] : 0);
@@ -263,29 +356,19 @@ __device__ SelectState block_select_coarse(const uint32_t (&key)[P], const bool 
         st.prefix = digit;
         st.krem = k - st.above;
     }
-    int nc = 0, nd = 0;
-    bool cd[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-        const uint32_t hi = key[q] >> st.shift;
-        cert[q] = valid[q] && hi > st.prefix;
-        cd[q] = valid[q] && hi == st.prefix;
-        nc += cert[q] ? 1 : 0;
-        nd += cd[q] ? 1 : 0;
-    }
-    int tot;
-    const int pre = block_excl_scan<NT>((nc << 16) | nd, sc, tot);
-    cert_rank = pre >> 16;
-    st.ncand = tot & 0xffff;
-    if (st.shift > 0) {
-        int cp = pre & 0xffff;
-#pragma unroll
-        for (int q = 0; q < P; ++q) {
-            if (cd[q]) cand[cp] = key[q];
-            cp += cd[q] ? 1 : 0;
-        }
-    }
-    lds_barrier();
+    return st;
+}
+
+// Coarse digit.  cert[q] / cand[q] classify each key; candidates go to `cand`
+// in index order (only when digits remain to be resolved).  `cert_rank` is the
+// index-order rank of this thread's first certain key; st.above = certain keys.
+// Requires 1 <= k <= number of valid keys.
+template <int P, int NT>
+__device__ SelectState block_select_coarse(const uint32_t (&key)[P], const bool (&valid)[P], int k,
+                                           int nbits, bool (&cert)[P], int& cert_rank,
+                                           uint32_t* hist, int* sc, uint32_t* cand) {
+    SelectState st = block_coarse_bin<P, NT>(key, valid, k, nbits, hist, sc);
+    classify_prefix<P, NT>(key, valid, st, cert, cert_rank, sc, cand);
     return st;
 }
 
@@ -315,6 +398,32 @@ __device__ void block_select_refine(SelectState& st, const uint32_t* cand, uint3
     }
     T = st.prefix;
     cgt = st.above;
+}
+
+// The k-th largest key when few candidates remain: candidate i takes its rank
+// among the candidates by comparing with all of them (LDS broadcast reads).
+// Same results as block_select_refine; for st.ncand <= NT.
+template <int NT>
+__device__ void block_select_refine_small(const SelectState& st, const uint32_t* cand, uint32_t& T,
+                                          int& cgt, int* sc) {
+    const int i = threadIdx.x;
+    if (i < st.ncand) {
+        const uint32_t v = cand[i];
+        int gt = 0, ge = 0;
+        for (int j = 0; j < st.ncand; ++j) {
+            const uint32_t u = cand[j];
+            gt += u > v ? 1 : 0;
+            ge += u >= v ? 1 : 0;
+        }
+        if (gt < st.krem && st.krem <= ge) {   // equal values write equal words
+            sc[22] = (int)v;
+            sc[23] = gt;
+        }
+    }
+    lds_barrier();
+    T = (uint32_t)sc[22];
+    cgt = st.above + sc[23];
+    lds_barrier();
 }
 
 // Keep exactly k of the valid keys: every key > T and the lowest-index keys

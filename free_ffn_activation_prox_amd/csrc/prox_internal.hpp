@@ -10,6 +10,11 @@ namespace prox {
 constexpr int kInt4Group = 128;
 constexpr int kTileRowBytes = 128;   // bytes of one tile row of the proxy (one cache line)
 constexpr int kMaxW2Total = 512;     // upper bound on Stage-2 blocks per launch (all tokens)
+// Coarse histogram of the ranking keys that Stage 1 builds per token: the bin
+// of a key is its fp32 bit pattern >> 18 (keys are >= 0, so 13 bits: sign 0,
+// exponent, 5 mantissa bits; 32 bins per binade).
+constexpr int kGhShift = 18;
+constexpr int kGhBins = 1 << (31 - kGhShift);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int tile_channels(int kind) { return kind == 1 ? 64 : 128; }
@@ -36,7 +41,7 @@ inline int stage2_blocks(int batch, int k_ff, int n_cu) {
 
 // Workspace carve-up (byte offsets) for one (d, F, B, kind).
 struct WsLayout {
-    size_t key, ypart, total;
+    size_t key, ypart, gh, total;
 };
 inline WsLayout ws_layout(int d, int F, int B, int kind) {
     const int fp = f_pad_of(F, kind);
@@ -44,6 +49,7 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
     size_t o = 0;
     L.key = o;    o = align_up(o + (size_t)B * fp * 4, 256);
     L.ypart = o;  o = align_up(o + (size_t)B * stage2_blocks_max(B) * d * 4, 256);
+    L.gh = o;     o = align_up(o + (size_t)B * kGhBins * 4, 256);
     L.total = o;
     return L;
 }
@@ -52,12 +58,13 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
 hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d, int F,
                               const ProxyView& p, hipStream_t s);
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
-                         double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
+                         uint32_t* gh, double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
                          hipStream_t s);
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
-                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
-                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart,
-                         hipStream_t s);
-hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s);
+                         const uint16_t* wd, const float* key, const uint32_t* gh, int B, int d,
+                         int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask,
+                         float* ypart, hipStream_t s);
+hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, uint32_t* gh,
+                           hipStream_t s);
 
 }  // namespace prox

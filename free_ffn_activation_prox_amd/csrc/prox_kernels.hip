@@ -144,6 +144,7 @@ struct Stage1Args {
     int d, k_in;
     ProxyView p;
     float* key;          // [B][f_pad]
+    uint32_t* gh;        // [B][kGhBins] coarse key histogram (zero on entry)
     double* h_tap;       // [B][F] or null
     float* key_tap;      // [B][F] or null
     int32_t* in_idx_tap; // [B][k_in] or null
@@ -358,8 +359,8 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int k_in = a.k_in, d = a.d;
     uint32_t* list = dyn;                         // [k_in]
-    uint32_t* cand = dyn + k_in;                  // [d]
-    uint8_t* flags = reinterpret_cast<uint8_t*>(dyn + k_in + d);
+    uint32_t* cand = dyn + k_in;                  // [d + 64]
+    uint8_t* flags = reinterpret_cast<uint8_t*>(dyn + k_in + d + 64);
     const int nchunks = stage1_select<PX>(a, b, list, cand, flags, hist, sc, 6);
 
     const int slot = w * 8 + (l >> 3);
@@ -445,6 +446,8 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) 
                 const double h = g / (1.0 + exp(-g)) * u;
                 const float kf = (float)fabs(h);
                 a.key[(size_t)b * a.p.f_pad + j] = kf;
+                __hip_atomic_fetch_add(a.gh + (size_t)b * kGhBins + (__float_as_uint(kf) >> kGhShift), 1u,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (a.h_tap) a.h_tap[(size_t)b * a.p.F + j] = h;
                 if (a.key_tap) a.key_tap[(size_t)b * a.p.F + j] = kf;
             }
@@ -456,7 +459,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) 
 template <int KIND, int PX>
 static hipError_t go_stage1(const Stage1Args& a, int B, int n_cu, hipStream_t s) {
     const int tiles = a.p.f_pad / (KIND == 1 ? 64 : 128);
-    const size_t dyn = (size_t)(a.k_in + a.d) * 4 + (a.k_in + kChunk - 1) / kChunk + 16;
+    const size_t dyn = (size_t)(a.k_in + a.d + 64) * 4 + (a.k_in + kChunk - 1) / kChunk + 16;
     auto fn = k_stage1<KIND, PX>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
@@ -480,20 +483,16 @@ static hipError_t stage1_px(const Stage1Args& a, int B, int n_cu, hipStream_t s)
 }
 
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
-                         double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
+                         uint32_t* gh, double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
                          hipStream_t s) {
-    Stage1Args a{x, d, k_in, p, key, h_tap, key_tap, in_idx_tap};
+    Stage1Args a{x, d, k_in, p, key, gh, h_tap, key_tap, in_idx_tap};
     return p.kind == 1 ? stage1_px<1>(a, B, n_cu, s) : stage1_px<2>(a, B, n_cu, s);
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2.  grid (W2, B), block 512 (8 waves).
-//
-// Top-k: thread t holds key[p * 512 + t] (p < PK); fp32 keys of non-negative
-// values order like their bit patterns (31 bits).  Every block finds the same
-// kept set and the rank of each kept channel in ascending index order; block w
-// keeps ranks [w*k/W2, (w+1)*k/W2) in LDS, writes those entries of idx and the
-// mask bytes of channels [w*F/W2, (w+1)*F/W2).
+// Stage 2.  grid (W2, B), block 512 (8 waves).  Block w of token b owns the
+// channel range [w*F/W2, (w+1)*F/W2): it writes the mask bytes and idx
+// entries of that range and the partial y over the kept channels in it.
 //
 // Sparse SwiGLU: thread t covers columns r*4096 + 8t .. +8 (r < R) of every
 // row.  Channels go G at a time, double-buffered: the gate/up/down rows of the
@@ -507,43 +506,54 @@ struct Stage2Args {
     const uint16_t* wu_t;
     const uint16_t* wd;
     const float* key;     // [B][f_pad]
+    const uint32_t* gh;   // [B][kGhBins] key histogram from Stage 1
     int d, F, f_pad, k, W2;
     int32_t* idx;         // [B][k] or null
     uint8_t* mask;        // [B][F] or null
     float* ypart;         // [B][W2][d]
 };
 
-constexpr int kS2Threads = 1024;
+constexpr int kS2Threads = 512;
 
-// Column ownership inside a team of TEAM threads: thread tt covers columns
-// r * TEAM * 8 + tt * 8 .. +8 for r < R.
+// Thread t covers columns r * 4096 + 8t .. +8 (r < R) of every row.
 template <int R, int G>
 struct RowGroup {
     uint4 g[G][R], u[G][R], dn[G][R];
 };
 
-template <int R, int G, int TEAM>
-__device__ __forceinline__ void load_group(const Stage2Args& a, const int* chan, int n, int v0,
-                                           int team, int tt, RowGroup<R, G>& rg) {
-    constexpr int NTEAM = kS2Threads / TEAM;
+// Rows of list entries v0 .. v0 + G - 1 (buffer loads: the row offset is
+// scalar, the column offset `voff` is this thread's).  Loads are unconditional
+// so the compiler keeps them in flight: entries past `last` re-read entry
+// `last` (in cache; their h is zeroed), columns past d re-read column 0 (x is 0
+// there).
+struct RowRsrc {
+    __amdgpu_buffer_rsrc_t g, u, dn;
+};
+
+template <int R, int G>
+__device__ __forceinline__ void load_group(const RowRsrc& rs, const uint16_t* chan, int v0, int last,
+                                           uint32_t row_bytes, const uint32_t (&voff)[R],
+                                           RowGroup<R, G>& rg) {
 #pragma unroll
     for (int q = 0; q < G; ++q) {
-        const int v = team + (v0 + q) * NTEAM;     // teams take list entries in turn
-        const bool ok = v < n;
-        const int j = ok ? chan[v] : 0;
+        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)chan[min(v0 + q, last)]) * row_bytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int col = r * TEAM * 8 + tt * 8;
-            if (ok && col < a.d) {
-                const size_t off = (size_t)j * a.d + col;
-                rg.g[q][r] = *reinterpret_cast<const uint4*>(a.wg_t + off);
-                rg.u[q][r] = *reinterpret_cast<const uint4*>(a.wu_t + off);
-                rg.dn[q][r] = *reinterpret_cast<const uint4*>(a.wd + off);
-            } else {
-                rg.g[q][r] = rg.u[q][r] = rg.dn[q][r] = make_uint4(0, 0, 0, 0);
-            }
+            rg.g[q][r] = buf_load16(rs.g, voff[r], soff);
+            rg.u[q][r] = buf_load16(rs.u, voff[r], soff);
+            rg.dn[q][r] = buf_load16(rs.dn, voff[r], soff);
         }
     }
+}
+
+// Materialise y here: no arithmetic on it moves across this point, and no
+// memory access either.
+template <int R>
+__device__ __forceinline__ void settle(float (&y)[R][8]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(y[r][e]) : : "memory");
 }
 
 __device__ __forceinline__ float dot8(const float (&x)[8], uint4 v, float acc) {
@@ -561,15 +571,14 @@ __device__ __forceinline__ void axpy8(float h, uint4 v, float (&y)[8]) {
     y[6] = fmaf(h, bf16_lo(v.w), y[6]); y[7] = fmaf(h, bf16_hi(v.w), y[7]);
 }
 
-// Gate/up dots of a group (fp32), reduced over the team's waves through LDS
-// (`red` = this parity's [team][wave][2G] buffer), then h = silu(g) u and the
-// W_down rows accumulated into the thread's part of y.
-template <int R, int G, int TEAM>
+// Gate/up dots of a group (fp32), reduced over the block's waves through LDS
+// (`red` = this parity's [wave][2G] buffer), then h = silu(g) u for the
+// `nvalid` leading entries and the W_down rows accumulated into y.
+template <int R, int G>
 __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const float (&xr)[R][8],
-                                              float (&yacc)[R][8], int n, int v0, float* red) {
-    constexpr int NTEAM = kS2Threads / TEAM;
-    constexpr int WPT = TEAM / kWave;      // waves per team
-    const int t = threadIdx.x, team = t / TEAM, tw = (t % TEAM) / kWave, l = t & 63;
+                                              float (&yacc)[R][8], int nvalid, float* red) {
+    constexpr int NW = kS2Threads / kWave;
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
     float pg[G], pu[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -582,12 +591,11 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
         pg[q] = wave_sum(ga);
         pu[q] = wave_sum(ua);
     }
-    float* my = red + (team * WPT) * (2 * G);
     if (l == 0) {
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-            my[tw * 2 * G + 2 * q] = pg[q];
-            my[tw * 2 * G + 2 * q + 1] = pu[q];
+            red[w * 2 * G + 2 * q] = pg[q];
+            red[w * 2 * G + 2 * q + 1] = pu[q];
         }
     }
     lds_barrier();
@@ -596,11 +604,11 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
     for (int q = 0; q < G; ++q) {
         float gs = 0.f, us = 0.f;
 #pragma unroll
-        for (int v = 0; v < WPT; ++v) {
-            gs += my[v * 2 * G + 2 * q];
-            us += my[v * 2 * G + 2 * q + 1];
+        for (int v = 0; v < NW; ++v) {
+            gs += red[v * 2 * G + 2 * q];
+            us += red[v * 2 * G + 2 * q + 1];
         }
-        h[q] = (team + (v0 + q) * NTEAM < n) ? gs / (1.f + expf(-gs)) * us : 0.f;
+        h[q] = q < nvalid ? gs / (1.f + expf(-gs)) * us : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < G; ++q)
@@ -609,43 +617,80 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
 }
 
 // ---------------------------------------------------------------------------
-// Stage 2.  grid (W2, B), block 1024 (16 waves), split into 1024 / TEAM teams
-// of TEAM threads; each team covers a whole row (R chunks of TEAM * 8 columns).
+// Stage 2 top-k.  A threshold bin (prefix at shift) splits the keys: those in
+// higher bins are kept for certain ("certain"), those in the bin are
+// "candidates".  The bin comes from the histogram Stage 1 built (else from the
+// block's own keys).  Thread t owns channels t*PK .. t*PK + PK - 1 for the
+// block-wide counts; the candidates go to LDS in index order and each gets
+// its rank (key descending, index ascending), so a candidate is kept when its
+// rank is below k - (certain keys).  The block's own range is handled one
+// channel per thread: its certain channels are listed and their first rows
+// requested as soon as the bin is known, before the candidates are resolved.
 //
-// Top-k: thread t owns channels t*PK .. t*PK + PK - 1 (keys staged through
-// LDS).  After the first radix digit, channels above the threshold bin are
-// certainly kept: block w takes its share of them (by rank in index order) and
-// issues their row loads at once; the candidates of the threshold bin are then
-// resolved (remaining digits, lowest index first among equal keys) while those
-// loads are in flight, and the block appends its share of the kept candidates.
-// Every block computes the same kept set, so the shares partition it.  Block w
-// also writes the idx entries of ranks [w*k/W2, (w+1)*k/W2) and the mask bytes
-// of channels [w*F/W2, (w+1)*F/W2).
-//
-// Sparse SwiGLU: the teams take the block's channel list in turn; each walks
-// its part G channels at a time with the next group's gate/up/down rows in
-// flight.  Finally the teams' partial y are added and written as the block's
-// partial.
+// The list: certain channels of the range in index order, then its kept
+// candidates in index order.  The first group holds the leading E = min(nc, G)
+// certain entries; the rest follow G at a time, each group's rows in flight
+// while the previous group is reduced and accumulated.
 // ---------------------------------------------------------------------------
-template <int PK, int R, int TEAM, int G>
-__global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
+constexpr int kSmallCand = 128;   // candidates ranked by direct comparison up to this many
+
+// Per-wave ballot counts of up to 4 predicates, then the block-wide exclusive
+// positions and totals.  `wc` = [4][8] ints of LDS; ends with a barrier that
+// makes `wc` reusable.
+template <int NP>
+__device__ __forceinline__ void block_ballot_pos(const bool (&p)[NP], int (*wc)[kS2Threads / kWave],
+                                                 int (&pos)[NP], int (&tot)[NP]) {
     constexpr int NW = kS2Threads / kWave;
-    constexpr int NTEAM = kS2Threads / TEAM;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint64_t m[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        m[i] = __ballot(p[i]);
+        if (lane == 0) wc[i][wv] = __popcll(m[i]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        int off = 0, all = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const int c = wc[i][v];
+            all += c;
+            off += v < wv ? c : 0;
+        }
+        pos[i] = off + lanes_below(m[i]);
+        tot[i] = all;
+    }
+    lds_barrier();
+}
+
+template <int PK, int R, int G>
+__global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
+    constexpr int NT = kS2Threads;
+    constexpr int NW = NT / kWave;
     extern __shared__ uint32_t dyn2[];
     __shared__ uint32_t hist[2048 + 64];
     __shared__ int sc[24];
+    __shared__ int wc[4][NW];
     __shared__ float red[2][NW * 2 * G];
 
     const int w = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-    const int team = t / TEAM, tt = t % TEAM;
     const int F = a.F, k = a.k, W2 = a.W2;
-    int* chan = reinterpret_cast<int*>(dyn2);            // [k / W2 + 2]
-    uint32_t* cand = dyn2 + (k + W2 - 1) / W2 + 2;       // [F]
-    // ---- x (this thread's columns) and the channel keys
+    const int r0 = (int)((long long)w * F / W2), r1 = (int)((long long)(w + 1) * F / W2);
+    const int L = r1 - r0;                                 // channels of this block's range
+    uint32_t* cand = dyn2;                                 // [F + 64] candidate keys, index order
+    uint16_t* chan = reinterpret_cast<uint16_t*>(dyn2 + F + 64);   // [cap + 64] the block's list
+    const float* keyb = a.key + (size_t)b * a.f_pad;
+
+    const uint32_t row_bytes = (uint32_t)a.d * 2u;
+    const uint32_t mat_bytes = (uint32_t)F * row_bytes;
+    const RowRsrc rs{make_rsrc(a.wg_t, mat_bytes), make_rsrc(a.wu_t, mat_bytes), make_rsrc(a.wd, mat_bytes)};
+    uint32_t voff[R];
     float xr[R][8], yacc[R][8];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int col = r * TEAM * 8 + tt * 8;
+        const int col = r * 4096 + t * 8;
+        voff[r] = col < a.d ? (uint32_t)col * 2u : 0u;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (col < a.d) v = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
         xr[r][0] = bf16_lo(v.x); xr[r][1] = bf16_hi(v.x);
@@ -656,105 +701,222 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
     }
     uint32_t kb[PK];
-    bool valid[PK];
-    load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(a.key + (size_t)b * a.f_pad), F, a.f_pad, kb, valid);
-    const bool all = k >= F;
-
-    // ---- certainly kept channels: this block's share, loads issued at once
-    bool cert[PK];
-    int crank;
-    SelectState st = classify<PK, kS2Threads>(kb, valid, k, all, 31, cert, crank, hist, sc, cand);
-    const int c_all = st.above;
-    const int c0 = (int)((long long)w * c_all / W2), c1 = (int)((long long)(w + 1) * c_all / W2);
-    const int cbase = crank;
+    {
+        bool valid[PK];
+        load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
+        // keys past F: negative as int, below every bin of a valid key
 #pragma unroll
-    for (int q = 0; q < PK; ++q) {
-        if (cert[q] && crank >= c0 && crank < c1) chan[crank - c0] = t * PK + q;
-        crank += cert[q] ? 1 : 0;
+        for (int q = 0; q < PK; ++q) kb[q] = valid[q] ? kb[q] : 0x80000000u;
     }
-    const int nc = c1 - c0;
-    lds_barrier();
-    RowGroup<R, G> cur, nxt;
-    const bool early = nc >= G * NTEAM;           // the first group lies in the certain part
-    if (early) load_group<R, G, TEAM>(a, chan, nc, 0, team, tt, cur);
+    // the first NT channels of the range, one per thread
+    uint32_t own0 = t < L ? __float_as_uint(keyb[r0 + t]) : 0u;
+    if (t == 0) chan[0] = 0;                               // row 0 stands in for an empty list
 
-    // ---- resolve the candidates while those loads are in flight
-    uint32_t T = 0;
-    int cgt = 0;
-    if (!all && k > 0) block_select_refine<kS2Threads>(st, cand, T, cgt, hist, sc);
-    bool on[PK];
-    int pos[PK];
-    block_keep_and_rank<PK, kS2Threads>(kb, valid, all, k, T, cgt, on, pos, sc);
-    // kept candidates: rank among them = rank among all kept - certain keys before
-    const int s_all = k - c_all;
-    const int s0 = (int)((long long)w * s_all / W2), s1 = (int)((long long)(w + 1) * s_all / W2);
-    const int r0 = (int)((long long)w * k / W2), r1 = (int)((long long)(w + 1) * k / W2);
-    const int m0 = (int)((long long)w * F / W2), m1 = (int)((long long)(w + 1) * F / W2);
-    int cb = cbase;
+    // ---- threshold bin
+    const bool all = k >= F, none = k == 0;
+    SelectState st{0u, 0, 0, 0, 0};
+    if (!all && !none) {
+        if (!block_hist_bin<NT, kGhBins>(a.gh + (size_t)b * kGhBins, k, F, kGhShift, sc, st)) {
+            bool valid[PK];
 #pragma unroll
-    for (int q = 0; q < PK; ++q) {
-        const int j = t * PK + q;
-        if (on[q] && !cert[q]) {
-            const int sr = pos[q] - cb;
-            if (sr >= s0 && sr < s1) chan[nc + sr - s0] = j;
+            for (int q = 0; q < PK; ++q) valid[q] = (int)kb[q] >= 0;
+            st = block_coarse_bin<PK, NT>(kb, valid, k, 31, hist, sc);
         }
-        cb += cert[q] ? 1 : 0;
-        if (a.idx && on[q] && pos[q] >= r0 && pos[q] < r1) a.idx[(size_t)b * k + pos[q]] = j;
-        if (a.mask && valid[q] && j >= m0 && j < m1) a.mask[(size_t)b * F + j] = on[q] ? 1 : 0;
     }
-    const int n = nc + (s1 - s0);
-    lds_barrier();
+    // bin of a key = (int)key >> shift: certain above cert_gt, candidate at
+    // cand_eq (keep-all: every valid key certain; keep-none: nothing)
+    const int shift = all || none ? 31 : st.shift;
+    const int cert_gt = all ? -1 : (none ? 0x7fffffff : (int)st.prefix);
+    const int cand_eq = all || none ? -2 : (int)st.prefix;
+    auto is_cert = [&](uint32_t v) { return ((int)v >> shift) > cert_gt; };
+    auto is_cand = [&](uint32_t v) { return ((int)v >> shift) == cand_eq; };
 
-    // ---- sparse SwiGLU over the block's channels, two groups in flight
-    const int per_team = (n + NTEAM - 1) / NTEAM;
-    const int groups = (per_team + G - 1) / G;     // same trip count in every team
-    if (!early) load_group<R, G, TEAM>(a, chan, n, 0, team, tt, cur);
-    for (int gi = 0; gi < groups; gi += 2) {
-        load_group<R, G, TEAM>(a, chan, n, (gi + 1) * G, team, tt, nxt);
-        consume_group<R, G, TEAM>(cur, xr, yacc, n, gi * G, red[0]);
-        if (gi + 1 >= groups) break;
-        load_group<R, G, TEAM>(a, chan, n, (gi + 2) * G, team, tt, cur);
-        consume_group<R, G, TEAM>(nxt, xr, yacc, n, (gi + 1) * G, red[1]);
+    // ---- block-wide counts: certain keys (high half), candidates (low half);
+    // the exclusive scan gives each thread the index-order rank of its first
+    // certain key and its first candidate
+    int ncert_t = 0, nd = 0;
+#pragma unroll
+    for (int q = 0; q < PK; ++q) {
+        ncert_t += is_cert(kb[q]) ? 1 : 0;
+        nd += is_cand(kb[q]) ? 1 : 0;
     }
-    // ---- add the teams' partial y (teams > 0 go through LDS) and write
-    if constexpr (NTEAM > 1) {
-        lds_barrier();                                  // the channel list is dead
-        float* ybuf = reinterpret_cast<float*>(dyn2);   // [NTEAM - 1][TEAM][R * 8]
-        if (team > 0) {
+    int tot;
+    const uint32_t pre = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)ncert_t << 16) | (uint32_t)nd), sc, tot);
+    const int ncand = (int)((uint32_t)tot & 0xffffu);
+    const int C = (int)((uint32_t)tot >> 16);            // certain keys in all
+    const int crank0 = (int)(pre >> 16);
+    // this block's share of the certain keys: ranks [c0, c1)
+    const int c0 = (int)((long long)w * C / W2), c1 = (int)((long long)(w + 1) * C / W2);
+    const int nc = c1 - c0;
+    {
+        // candidates to cand[] and this block's certain share to chan[];
+        // lanes with nothing to write store to a per-lane dummy word
+        const int lane = t & 63;
+        uint32_t* cdummy = cand + F + lane;
+        uint16_t* sdummy = chan + (k + W2 - 1) / W2 + 2 + lane;
+        const bool share = crank0 < c1 && crank0 + ncert_t > c0;
+        const bool owns_r0 = t == r0 / PK;
+        if (nd > 0 || share || owns_r0) {
+            int cp = (int)(pre & 0xffffu), cr = crank0, cp_r0 = 0, cr_r0 = 0;
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ybuf[((team - 1) * TEAM + tt) * R * 8 + r * 8 + e] = yacc[r][e];
+            for (int q = 0; q < PK; ++q) {
+                const bool ce = is_cert(kb[q]), cd = is_cand(kb[q]);
+                const bool at_r0 = t * PK + q == r0;
+                cp_r0 = at_r0 ? cp : cp_r0;                // counts before the range
+                cr_r0 = at_r0 ? cr : cr_r0;
+                *(cd ? cand + cp : cdummy) = kb[q];
+                *(ce && cr >= c0 && cr < c1 ? chan + (cr - c0) : sdummy) = (uint16_t)(t * PK + q);
+                cp += cd ? 1 : 0;
+                cr += ce ? 1 : 0;
+            }
+            if (owns_r0) {
+                sc[16] = cp_r0;
+                sc[18] = cr_r0;
+            }
+        }
+    }
+    lds_barrier();
+    const int cs = sc[16];                                 // candidates before the range
+    const int cert_before = sc[18];                        // certain keys before the range
+    const int E = min(nc, G);
+    RowGroup<R, G> cur, nxt;
+    load_group<R, G>(rs, chan, 0, max(E - 1, 0), row_bytes, voff, cur);
+
+    // ---- resolve the candidates while those loads are in flight: cand[i]
+    // gets bit 31 when kept
+    if (ncand > 0) {
+        const int need = st.krem;                         // candidates to keep
+        if (ncand <= kSmallCand) {
+            bool kept = false;
+            if (t < ncand) {
+                const uint32_t v = cand[t];
+                int rank = 0;
+                for (int i = 0; i < ncand; ++i) {
+                    const uint32_t u = cand[i];
+                    rank += (u > v || (u == v && i < t)) ? 1 : 0;
+                }
+                kept = rank < need;
+            }
+            lds_barrier();
+            if (kept) cand[t] |= 0x80000000u;
+        } else {
+            SelectState s2 = st;
+            s2.ncand = ncand;
+            uint32_t T;
+            int cgt;
+            block_select_refine<NT>(s2, cand, T, cgt, hist, sc);
+            // kept: above T, or equal to T and among the first k - cgt equal ones
+            const int eq_need = k - cgt;
+            int eq_run = 0;
+            for (int i0 = 0; i0 < ncand; i0 += NT) {
+                const int i = i0 + t;
+                const uint32_t v = i < ncand ? cand[i] : 0u;
+                bool p[1] = {i < ncand && v == T};
+                int pos[1], tt[1];
+                block_ballot_pos<1>(p, wc, pos, tt);
+                if (i < ncand && (v > T || (p[0] && eq_run + pos[0] < eq_need))) cand[i] = v | 0x80000000u;
+                eq_run += tt[0];
+            }
         }
         lds_barrier();
-        if (team == 0) {
-            for (int m = 1; m < NTEAM; ++m)
+    }
+    // ---- kept candidates: this block's share (ranks [s0, s1) among them, in
+    // index order) goes after its certain entries; count those before the range
+    int nks = 0, kc_before = 0;
+    {
+        int run = 0;
+        for (int i0 = 0; i0 < ncand; i0 += NT) {
+            const int i = i0 + t;
+            const bool kept = i < ncand && (cand[i] >> 31) != 0;
+            bool p[2] = {kept, kept && i < cs};
+            int pos[2], tt[2];
+            block_ballot_pos<2>(p, wc, pos, tt);
+            pos[0] += run;
+            run += tt[0];
+            kc_before += tt[1];
+            if (kept) cand[i] = 0x80000000u | (uint32_t)pos[0];   // the flag, and the rank
+        }
+        if (ncand > 0) lds_barrier();
+        const int KC = run;
+        const int s0 = (int)((long long)w * KC / W2), s1 = (int)((long long)(w + 1) * KC / W2);
+        nks = s1 - s0;
+        // the owners of the candidates place this block's share
+        if (nd > 0 && s1 > s0) {
+            uint16_t* sdummy = chan + (k + W2 - 1) / W2 + 2 + (t & 63);
+            int cp = (int)(pre & 0xffffu);
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) yacc[r][e] += ybuf[((m - 1) * TEAM + tt) * R * 8 + r * 8 + e];
+            for (int q = 0; q < PK; ++q) {
+                const bool cd = is_cand(kb[q]);
+                const uint32_t v = cand[cp];                // cp <= ncand: in bounds
+                const int r = (int)(v & 0x7fffffffu);
+                *(cd && (v >> 31) && r >= s0 && r < s1 ? chan + (nc + r - s0) : sdummy) = (uint16_t)(t * PK + q);
+                cp += cd ? 1 : 0;
+            }
         }
     }
-    if (team == 0) {
-        float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
+    const int kept_before = cert_before + kc_before;
+
+    // ---- the range: kept flags, idx and mask
+    if (a.idx || a.mask) {
+        int nk = 0, nd_run = 0;
+        for (int c0r = 0; c0r < L; c0r += NT) {
+            const int j = r0 + c0r + t;
+            const bool in = c0r + t < L;
+            const uint32_t v = c0r == 0 ? own0 : (in ? __float_as_uint(keyb[j]) : 0u);
+            bool p1[1] = {in && is_cand(v)};
+            int pos1[1], t1[1];
+            block_ballot_pos<1>(p1, wc, pos1, t1);
+            const bool kc = p1[0] && (cand[cs + nd_run + pos1[0]] >> 31) != 0;
+            bool p2[1] = {in && (is_cert(v) || kc)};
+            int pos2[1], t2[1];
+            block_ballot_pos<1>(p2, wc, pos2, t2);
+            if (p2[0] && a.idx) a.idx[(size_t)b * k + kept_before + nk + pos2[0]] = j;
+            if (in && a.mask) a.mask[(size_t)b * F + j] = p2[0] ? 1 : 0;
+            nd_run += t1[0];
+            nk += t2[0];
+        }
+    }
+    const int nkc = nks;
+    const int n = nc + nkc;
+    lds_barrier();
+
+    // ---- sparse SwiGLU: group 0 = entries [0, E), then [E, n) G at a time.
+    // The loads are unconditional and the loop has no exit from its middle:
+    // on any path that merges pending and completed loads the compiler drains
+    // every load and the overlap is lost.  After the last group, `cur` re-reads
+    // the last entry (cache hits) and is left unused.
+    const int rest = n - E;
+    const int groups = 1 + (rest + G - 1) / G;
+    const int last = max(n - 1, 0);
+    int gi = 0;
+    for (; gi + 1 < groups; gi += 2) {
+        load_group<R, G>(rs, chan, E + gi * G, last, row_bytes, voff, nxt);
+        consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
+        // The accumulation into y must finish before `cur` is reloaded: if the
+        // compiler sinks it below the reloads, the old and new `cur` overlap
+        // and the loop-carried registers need a copy that waits for the loads.
+        settle(yacc);
+        load_group<R, G>(rs, chan, E + (gi + 1) * G, last, row_bytes, voff, cur);
+        consume_group<R, G>(nxt, xr, yacc, min(G, rest - gi * G), red[1]);
+        settle(yacc);
+    }
+    if (gi < groups) consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
+    float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int col = r * TEAM * 8 + tt * 8;
-            if (col < a.d) {
-                *reinterpret_cast<float4*>(dst + col) = make_float4(yacc[r][0], yacc[r][1], yacc[r][2], yacc[r][3]);
-                *reinterpret_cast<float4*>(dst + col + 4) = make_float4(yacc[r][4], yacc[r][5], yacc[r][6], yacc[r][7]);
-            }
+    for (int r = 0; r < R; ++r) {
+        const int col = r * 4096 + t * 8;
+        if (col < a.d) {
+            *reinterpret_cast<float4*>(dst + col) = make_float4(yacc[r][0], yacc[r][1], yacc[r][2], yacc[r][3]);
+            *reinterpret_cast<float4*>(dst + col + 4) = make_float4(yacc[r][4], yacc[r][5], yacc[r][6], yacc[r][7]);
         }
     }
 }
 
-template <int PK, int R, int TEAM, int G>
+template <int PK, int R, int G>
 static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
-    constexpr int NTEAM = kS2Threads / TEAM;
-    const size_t lists = ((size_t)(a.k + a.W2 - 1) / a.W2 + 2 + (size_t)a.F) * 4;
-    const size_t ybuf = NTEAM > 1 ? (size_t)(NTEAM - 1) * TEAM * R * 8 * 4 : 0;
-    const size_t dyn = lists > ybuf ? lists : ybuf;
-    auto fn = k_stage2<PK, R, TEAM, G>;
+    const int cap = (a.k + a.W2 - 1) / a.W2 + 2;          // list length bound: ceil(C/W2) + ceil(KC/W2)
+    const size_t dyn = ((size_t)a.F + 64) * 4 + ((size_t)cap + 64) * 2;
+    auto fn = k_stage2<PK, R, G>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -763,60 +925,82 @@ static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int R, int TEAM, int G>
+template <int R, int G>
 static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
     const int per = (a.F + kS2Threads - 1) / kS2Threads;
-    if (per <= 4) return go_stage2<4, R, TEAM, G>(a, B, s);
-    if (per <= 8) return go_stage2<8, R, TEAM, G>(a, B, s);
-    if (per <= 12) return go_stage2<12, R, TEAM, G>(a, B, s);
-    if (per <= 16) return go_stage2<16, R, TEAM, G>(a, B, s);
-    if (per <= 20) return go_stage2<20, R, TEAM, G>(a, B, s);
-    if (per <= 24) return go_stage2<24, R, TEAM, G>(a, B, s);
-    if (per <= 28) return go_stage2<28, R, TEAM, G>(a, B, s);
-    return go_stage2<32, R, TEAM, G>(a, B, s);
+    if (per <= 4) return go_stage2<4, R, G>(a, B, s);
+    if (per <= 8) return go_stage2<8, R, G>(a, B, s);
+    if (per <= 16) return go_stage2<16, R, G>(a, B, s);
+    if (per <= 24) return go_stage2<24, R, G>(a, B, s);
+    if (per <= 32) return go_stage2<32, R, G>(a, B, s);
+    if (per <= 40) return go_stage2<40, R, G>(a, B, s);
+    if (per <= 48) return go_stage2<48, R, G>(a, B, s);
+    if (per <= 56) return go_stage2<56, R, G>(a, B, s);
+    return go_stage2<64, R, G>(a, B, s);
 }
 
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
-                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
-                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart,
-                         hipStream_t s) {
-    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart};
-    if (d <= 4096) return stage2_pk<1, 512, 2>(a, B, s);
-    if (d <= 8192) return stage2_pk<1, 1024, 2>(a, B, s);
-    return stage2_pk<2, 1024, 1>(a, B, s);
+                         const uint16_t* wd, const float* key, const uint32_t* gh, int B, int d,
+                         int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask,
+                         float* ypart, hipStream_t s) {
+    Stage2Args a{x, wg_t, wu_t, wd, key, gh, d, F, f_pad, k_ff, W2, idx, mask, ypart};
+    if (d <= 4096) return stage2_pk<1, 4>(a, B, s);
+    if (d <= 8192) return stage2_pk<2, 2>(a, B, s);
+    return stage2_pk<4, 1>(a, B, s);
 }
 
 // ---------------------------------------------------------------------------
-// y = sum of the W2 block partials, fixed order.  grid (ceil(d / 64), B),
-// block 256: lane = column, wave q sums partials q, q+4, ... into 8 running
-// sums (independent loads in flight), then the waves combine in LDS.
+// y = sum of the W2 block partials, fixed order, and the token's key
+// histogram back to zero for the next call.  grid (ceil(d / 32), B), block
+// 256: thread (g = t / 8, c = t % 8) sums partials g, g + 32, ... of columns
+// 4c .. 4c + 3 of the block's 32 (all of its loads in flight at once), then
+// the 32 groups are combined in LDS in a fixed tree.
 // ---------------------------------------------------------------------------
+constexpr int kRedCols = 32;
+constexpr int kRedGroups = 32;
+constexpr int kRedMax = kMaxW2Total / kRedGroups;   // partials per thread
+
 __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypart, int d, int W2,
-                                                  float* __restrict__ y) {
-    __shared__ float acc[4][64];
-    const int b = blockIdx.y;
-    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int col = blockIdx.x * 64 + lane;
-    float s[8];
+                                                  float* __restrict__ y, uint32_t* __restrict__ gh) {
+    __shared__ float4 acc[kRedGroups][kRedCols / 4];
+    const int b = blockIdx.y, t = threadIdx.x;
+    const int g = t >> 3, c = t & 7;
+    const int col = blockIdx.x * kRedCols + 4 * c;
+    const bool in = col < d;                       // d % 8 == 0, so a quad is all in or all out
+    const float* src = ypart + (size_t)b * W2 * d + (in ? col : 0);
+    float4 v[kRedMax];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s[u] = 0.f;
-    if (col < d) {
-        const float* src = ypart + (size_t)b * W2 * d + col;
-        int wv = q;
-        for (; wv + 28 < W2; wv += 32) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s[u] += src[(size_t)(wv + 4 * u) * d];
-        }
-        for (int u = 0; wv < W2; wv += 4, ++u) s[u & 7] += src[(size_t)wv * d];
+    for (int u = 0; u < kRedMax; ++u) {
+        const int wv = g + u * kRedGroups;
+        v[u] = wv < W2 ? *reinterpret_cast<const float4*>(src + (size_t)wv * d) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float tot = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-    acc[q][lane] = tot;
+    float4 s4 = v[0];
+#pragma unroll
+    for (int u = 1; u < kRedMax; ++u) {
+        s4.x += v[u].x; s4.y += v[u].y; s4.z += v[u].z; s4.w += v[u].w;
+    }
+    acc[g][c] = s4;
     __syncthreads();
-    if (q == 0 && col < d) y[(size_t)b * d + col] = (acc[0][lane] + acc[1][lane]) + (acc[2][lane] + acc[3][lane]);
+#pragma unroll
+    for (int h = kRedGroups / 2; h >= 1; h >>= 1) {
+        if (g < h) {
+            const float4 o = acc[g + h][c];
+            s4.x += o.x; s4.y += o.y; s4.z += o.z; s4.w += o.w;
+            acc[g][c] = s4;
+        }
+        __syncthreads();
+    }
+    if (g == 0 && in) *reinterpret_cast<float4*>(y + (size_t)b * d + col) = s4;
+    // histogram: this token's bins, spread over the token's blocks
+    uint32_t* hb = gh + (size_t)b * kGhBins;
+    for (int i = (blockIdx.x * 256 + t) * 4; i < kGhBins; i += gridDim.x * 256 * 4)
+        *reinterpret_cast<uint4*>(hb + i) = make_uint4(0, 0, 0, 0);
 }
 
-hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s) {
-    hipLaunchKernelGGL(k_reduce_y, dim3((d + 63) / 64, B), dim3(256), 0, s, ypart, d, W2, y);
+hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, uint32_t* gh,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(k_reduce_y, dim3((d + kRedCols - 1) / kRedCols, B), dim3(256), 0, s, ypart, d,
+                       W2, y, gh);
     return hipGetLastError();
 }
 
