@@ -1,5 +1,7 @@
 // Prox C ABI: host-side validation, workspace carve-up and launch sequence.
 // Every check runs before the first launch, so an error return enqueues nothing.
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -85,6 +87,13 @@ int device_cus() {
         cache[dev] = n;
     }
     return cache[dev];
+}
+
+// A tag per call for the Stage-1 arrival counters: counters left by any
+// earlier call (this process or another, or never cleared) carry another tag.
+uint32_t next_call_tag() {
+    static std::atomic<uint32_t> tag{(uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
+    return tag.fetch_add(1u, std::memory_order_relaxed);
 }
 
 }  // namespace
@@ -180,8 +189,12 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
 
     hipError_t e = mark(0);
     if (e != hipSuccess) return hip_fail(e, "event record");
-    e = launch_stage1(xb, batch, d, k_in, pv, key, gh, taps ? taps->h_hat : nullptr,
-                      taps ? taps->key : nullptr, taps ? taps->in_idx : nullptr, n_cu, s);
+    const S1Geom g1 = s1_geom(k_in, F, p->kind, batch, n_cu);
+    double* part = reinterpret_cast<double*>(ws + L.part);
+    unsigned long long* tcnt = reinterpret_cast<unsigned long long*>(ws + L.tcnt);
+    e = launch_stage1(xb, batch, d, k_in, pv, key, gh, part, tcnt, next_call_tag(), g1,
+                      taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr,
+                      taps ? taps->in_idx : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "stage 1");
     if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_stage2(xb, static_cast<const uint16_t*>(w->w_gate_t),

@@ -159,6 +159,36 @@ __device__ __forceinline__ int block_max(int v, int* lds) {
     return m;
 }
 
+// Per-wave ballot counts of up to 4 predicates, then the block-wide exclusive
+// positions (in thread order) and totals.  `wc` = [4][NT / 64] ints of LDS;
+// ends with a barrier that makes `wc` reusable.
+template <int NT, int NP>
+__device__ __forceinline__ void block_ballot_pos(const bool (&p)[NP], int (*wc)[NT / kWave],
+                                                 int (&pos)[NP], int (&tot)[NP]) {
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint64_t m[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        m[i] = __ballot(p[i]);
+        if (lane == 0) wc[i][wv] = __popcll(m[i]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        int off = 0, all = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const int c = wc[i][v];
+            all += c;
+            off += v < wv ? c : 0;
+        }
+        pos[i] = off + lanes_below(m[i]);
+        tot[i] = all;
+    }
+    lds_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // Keys with contiguous ownership: thread t holds elements t*P .. t*P + P - 1,
 // read with 16-byte loads.  `readable` (a multiple of the vector width) bounds
@@ -198,18 +228,10 @@ __device__ __forceinline__ void load_u16_contig(const uint16_t* __restrict__ src
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide selection of the k largest of the valid keys (keys < 2^nbits),
-// ties to the lowest index (index of element (t, q) = t * P + q).
-//
-// 1) coarse: one radix digit of <= 11 bits in a window that starts at the
-//    highest bit set in any key, so the keys spread over as many bins as the
-//    data allow.  Keys whose digit is above the threshold bin are certainly
-//    kept ("certain"); keys in the threshold bin are "candidates", written to
-//    an LDS array.  A caller can start work on the certain keys here.
-// 2) refine: the remaining digits over the candidate array only.
-// 3) keep: exact flags and ranks in index order for every key.
-// LDS: `hist` >= 2049 uints, `sc` >= 24 ints, `cand` >= number of candidates
-// (at most the number of valid keys) + 64.  Every thread calls every step.
+// Block-wide radix selection pieces.  A threshold bin splits the keys: keys
+// in higher bins are kept for certain, keys in the bin are candidates that the
+// remaining (lower) bits and then the index order decide.  Every thread calls
+// every step.
 // ---------------------------------------------------------------------------
 struct SelectState {
     uint32_t prefix;   // resolved high bits of the k-th largest key
@@ -245,41 +267,6 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int krem,
     lds_barrier();
     digit = (uint32_t)sc[20];
     above = sc[21];
-    lds_barrier();
-}
-
-// With the resolved digit (st.prefix at st.shift) known: cert[q] = key above
-// the threshold bin, candidates (digit == prefix) go to `cand` in index order
-// when bits remain below the digit.  Sets cert_rank (index-order rank of this
-// thread's first certain key) and st.ncand.
-template <int P, int NT>
-__device__ __forceinline__ void classify_prefix(const uint32_t (&key)[P], const bool (&valid)[P],
-                                                SelectState& st, bool (&cert)[P], int& cert_rank,
-                                                int* sc, uint32_t* cand) {
-    int nc = 0, nd = 0;
-    bool cd[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-        const uint32_t hi = key[q] >> st.shift;
-        cert[q] = valid[q] && hi > st.prefix;
-        cd[q] = valid[q] && hi == st.prefix;
-        nc += cert[q] ? 1 : 0;
-        nd += cd[q] ? 1 : 0;
-    }
-    int tot;
-    const int pre = block_excl_scan<NT>((nc << 16) | nd, sc, tot);
-    cert_rank = pre >> 16;
-    st.ncand = tot & 0xffff;
-    if (st.shift > 0) {
-        // branch-free: lanes without a candidate write a per-lane dummy word
-        int cp = pre & 0xffff;
-        uint32_t* dummy = cand + st.ncand + (threadIdx.x & 63);
-#pragma unroll
-        for (int q = 0; q < P; ++q) {
-            *(cd[q] ? cand + cp : dummy) = key[q];
-            cp += cd[q] ? 1 : 0;
-        }
-    }
     lds_barrier();
 }
 
@@ -359,19 +346,6 @@ __device__ SelectState block_coarse_bin(const uint32_t (&key)[P], const bool (&v
     return st;
 }
 
-// Coarse digit.  cert[q] / cand[q] classify each key; candidates go to `cand`
-// in index order (only when digits remain to be resolved).  `cert_rank` is the
-// index-order rank of this thread's first certain key; st.above = certain keys.
-// Requires 1 <= k <= number of valid keys.
-template <int P, int NT>
-__device__ SelectState block_select_coarse(const uint32_t (&key)[P], const bool (&valid)[P], int k,
-                                           int nbits, bool (&cert)[P], int& cert_rank,
-                                           uint32_t* hist, int* sc, uint32_t* cand) {
-    SelectState st = block_coarse_bin<P, NT>(key, valid, k, nbits, hist, sc);
-    classify_prefix<P, NT>(key, valid, st, cert, cert_rank, sc, cand);
-    return st;
-}
-
 // Remaining digits over the candidate array.  T = the k-th largest key,
 // cgt = number of keys > T.
 template <int NT>
@@ -398,65 +372,6 @@ __device__ void block_select_refine(SelectState& st, const uint32_t* cand, uint3
     }
     T = st.prefix;
     cgt = st.above;
-}
-
-// The k-th largest key when few candidates remain: candidate i takes its rank
-// among the candidates by comparing with all of them (LDS broadcast reads).
-// Same results as block_select_refine; for st.ncand <= NT.
-template <int NT>
-__device__ void block_select_refine_small(const SelectState& st, const uint32_t* cand, uint32_t& T,
-                                          int& cgt, int* sc) {
-    const int i = threadIdx.x;
-    if (i < st.ncand) {
-        const uint32_t v = cand[i];
-        int gt = 0, ge = 0;
-        for (int j = 0; j < st.ncand; ++j) {
-            const uint32_t u = cand[j];
-            gt += u > v ? 1 : 0;
-            ge += u >= v ? 1 : 0;
-        }
-        if (gt < st.krem && st.krem <= ge) {   // equal values write equal words
-            sc[22] = (int)v;
-            sc[23] = gt;
-        }
-    }
-    lds_barrier();
-    T = (uint32_t)sc[22];
-    cgt = st.above + sc[23];
-    lds_barrier();
-}
-
-// Keep exactly k of the valid keys: every key > T and the lowest-index keys
-// equal to T (all = keep every valid key).  pos[q] is the rank of a kept key
-// in ascending index order.  One block scan of the packed per-thread counts
-// (keys > T in the high half, keys == T in the low half: fewer than k <= 2^15
-// keys exceed T and at most 2^15 equal it, so the packed sum stays below 2^31).
-// Returns the number kept.  `sc` >= 16 ints of LDS.
-template <int P, int NT>
-__device__ int block_keep_and_rank(const uint32_t (&key)[P], const bool (&valid)[P], bool all,
-                                   int k, uint32_t T, int cgt, bool (&on)[P], int (&pos)[P],
-                                   int* sc) {
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-        gt += (valid[q] && (all || key[q] > T)) ? 1 : 0;
-        eq += (valid[q] && !all && key[q] == T) ? 1 : 0;
-    }
-    int tot;
-    // keep-all counts may reach 2^15, so they are scanned unpacked
-    const int pre = block_excl_scan<NT>(all ? gt : ((gt << 16) | eq), sc, tot);
-    const int need = all ? 0 : k - cgt;
-    int eq_before = all ? 0 : (pre & 0xffff);
-    int kept = all ? pre : (pre >> 16) + min(eq_before, need);
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-        const bool e = valid[q] && !all && key[q] == T;
-        on[q] = valid[q] && k > 0 && (all || key[q] > T || (e && eq_before < need));
-        eq_before += e ? 1 : 0;
-        pos[q] = kept;
-        kept += on[q] ? 1 : 0;
-    }
-    return all ? tot : (tot >> 16) + min(tot & 0xffff, need);
 }
 
 }  // namespace prox

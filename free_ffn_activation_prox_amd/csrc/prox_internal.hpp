@@ -10,6 +10,8 @@ namespace prox {
 constexpr int kInt4Group = 128;
 constexpr int kTileRowBytes = 128;   // bytes of one tile row of the proxy (one cache line)
 constexpr int kMaxW2Total = 512;     // upper bound on Stage-2 blocks per launch (all tokens)
+constexpr int kMaxS1Total = 512;     // upper bound on Stage-1 blocks per launch (all tokens)
+constexpr int kPartChannels = 128;   // channels per partial-sum slot (the int4 tile width)
 // Coarse histogram of the ranking keys that Stage 1 builds per token: the bin
 // of a key is its fp32 bit pattern >> 18 (keys are >= 0, so 13 bits: sign 0,
 // exponent, 5 mantissa bits; 32 bins per binade).
@@ -39,9 +41,36 @@ inline int stage2_blocks(int batch, int k_ff, int n_cu) {
     return w < 1 ? 1 : w;
 }
 
+// Stage-1 work split: T = tiles * nch items (tile, chunk of 8 kept inputs),
+// nb1 blocks per token.
+struct S1Geom {
+    int tiles, nch, nb1;
+};
+inline int s1_blocks_max(int batch) {
+    int w = kMaxS1Total / batch;
+    return w < 1 ? 1 : w;
+}
+inline S1Geom s1_geom(int k_in, int F, int kind, int batch, int n_cu) {
+    S1Geom g;
+    g.tiles = f_pad_of(F, kind) / tile_channels(kind);
+    g.nch = k_in > 0 ? (k_in + 7) / 8 : 1;
+    int nb = n_cu / batch;
+    if (nb > s1_blocks_max(batch)) nb = s1_blocks_max(batch);
+    if (nb < 1) nb = 1;
+    // int8 tiles are cheap enough per row to be bound by the stream: with no
+    // more tiles than blocks each block takes one whole tile (no partial sums
+    // to combine).  int4 rows cost more arithmetic per byte: its items are
+    // always spread over every block.
+    if (kind == 1 && g.tiles < nb) nb = g.tiles;
+    const long long T = (long long)g.tiles * g.nch;
+    if (nb > T) nb = (int)T;
+    g.nb1 = nb;
+    return g;
+}
+
 // Workspace carve-up (byte offsets) for one (d, F, B, kind).
 struct WsLayout {
-    size_t key, ypart, gh, total;
+    size_t key, ypart, gh, part, tcnt, total;
 };
 inline WsLayout ws_layout(int d, int F, int B, int kind) {
     const int fp = f_pad_of(F, kind);
@@ -50,6 +79,8 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
     L.key = o;    o = align_up(o + (size_t)B * fp * 4, 256);
     L.ypart = o;  o = align_up(o + (size_t)B * stage2_blocks_max(B) * d * 4, 256);
     L.gh = o;     o = align_up(o + (size_t)B * kGhBins * 4, 256);
+    L.part = o;   o = align_up(o + (size_t)B * (fp / tile_channels(kind) + s1_blocks_max(B)) * 2 * kPartChannels * 8, 256);
+    L.tcnt = o;   o = align_up(o + (size_t)B * (fp / tile_channels(kind)) * 8, 256);
     L.total = o;
     return L;
 }
@@ -58,7 +89,8 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
 hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d, int F,
                               const ProxyView& p, hipStream_t s);
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
-                         uint32_t* gh, double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
+                         uint32_t* gh, double* part, unsigned long long* tcnt, uint32_t gen,
+                         const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
                          hipStream_t s);
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
                          const uint16_t* wd, const float* key, const uint32_t* gh, int B, int d,

@@ -1,13 +1,16 @@
 // Prox sparse SwiGLU FFN: gfx950 kernels.
 //
-// One forward = three launches (Prox, Abstract; SwiGLU as in PrunePath, §2.1, Eq. (1)):
-//   stage1   per (channel tile, token): input selection (top-k_in of |x|, redone in
-//            every block: x is a few KB), proxy GEMV over the kept rows of the tile,
-//            h~ = silu(g~) u~ in fp64 and the fp32 ranking key |h~|
-//   stage2   per (block, token): top-k of the keys (redone in every block: the keys
-//            are a few tens of KB), the block's slice of the ranked channel list,
-//            then for each of its channels the exact gate/up dots over the dense x,
-//            h = silu(g) u and h * W_down row into the block's partial y
+// One forward = four launches (Prox, Abstract; SwiGLU as in PrunePath, §2.1, Eq. (1)):
+//   stage1   per (block, token): input selection (top-k_in of |x|, redone in
+//            every block: x is a few KB), then the block's equal share of the
+//            (channel tile, kept-row chunk) items of the proxy GEMV
+//   score    per (channel tile, token): the tile's partial sums in a fixed
+//            order, h~ = silu(g~) u~ in fp64, the fp32 ranking key |h~| and a
+//            coarse histogram of the keys
+//   stage2   per (block, token): top-k of the keys (threshold bin from the
+//            histogram, redone in every block), the block's share of the kept
+//            channels, then for each of them the exact gate/up dots over the
+//            dense x, h = silu(g) u and h * W_down row into the block's partial y
 //   reduce   y = fixed-order sum of the block partials
 // plus the one-time proxy build.
 //
@@ -121,23 +124,33 @@ hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d,
 }
 
 // ---------------------------------------------------------------------------
-// Stage 1.  grid (tiles, B), block 512 (8 waves).
+// Stage 1.  grid (NB1, B), block 512 (8 waves).
 //
-// Input selection: thread t holds x[p * 512 + t] (p < PX); keys are the 15
-// magnitude bits of the bf16 value (monotone in |x|, -0 == +0).  The kept
-// inputs, ascending, go to LDS as (index << 16 | bf16 bits).
+// Work items: (tile, chunk) pairs, tile-major, chunk = 8 consecutive entries
+// of the token's kept-input list; block w takes items [w*T/NB1, (w+1)*T/NB1)
+// of the T = tiles * nch items, so every compute unit streams the same number
+// of proxy rows whatever the tile count.  A block's share of a tile is a
+// "segment"; its partial gate/up sums go to `part` and the score kernel adds
+// the segments of each tile in segment order.
 //
-// GEMV: the kept list is cut into chunks of 8 consecutive entries; row slot s
-// (= 8 * wave + lane / 8, 64 slots) takes chunks s, s + 64, ...; lane % 8 picks
-// a 16-byte block of the tile row (int8: 8 gate + 8 up codes; int4: 16 + 16).
-// int8 chunks accumulate in fp32 when the chunk's x exponents span <= 6
-// binades: every product x * q is then a multiple of 2^(e_lo - 7) below
-// 2^(e_hi + 8), so the partial sums of <= 8 products are integers below 2^24 in
-// those units and every fp32 step is exact; the chunk sum is then added to the
-// fp64 accumulator.  Other chunks accumulate in fp64 directly.  int4
-// accumulates in fp64 and scales each 128-input group's inner sum when the
-// group changes.  The slots are reduced with lane shuffles and LDS in a fixed
-// order, so the result is deterministic.
+// Input selection: thread t holds x[t*PX .. t*PX + PX - 1]; keys are the 15
+// magnitude bits of the bf16 value (monotone in |x|, -0 == +0).  Keys in bins
+// (key >> 4) above the threshold bin are kept for certain; the candidates of
+// that bin are ranked (key descending, index ascending) by direct comparison.
+// The list in LDS holds (index << 16 | bf16 bits): the certain inputs in index
+// order, then the kept candidates in index order (the GEMV sums over the list,
+// so only the set matters).
+//
+// GEMV: row slot s (= 8 * wave + lane / 8, 64 slots) takes the segment's chunks
+// s, s + 64, ...; lane % 8 picks a 16-byte block of the tile row (int8: 8 gate
+// + 8 up codes; int4: 16 + 16).  int8 chunks accumulate in fp32 when the
+// chunk's x exponents span <= 6 binades: every product x * q is then a multiple
+// of 2^(e_lo - 7) below 2^(e_hi + 8), so the partial sums of <= 8 products are
+// integers below 2^24 in those units and every fp32 step is exact; the chunk
+// sum is then added to the fp64 accumulator.  Other chunks accumulate in fp64
+// directly.  int4 accumulates in fp64 and scales each 128-input group's inner
+// sum when the group changes.  The slots are reduced with lane shuffles and
+// LDS in a fixed order, so the result is deterministic.
 // ---------------------------------------------------------------------------
 struct Stage1Args {
     const uint16_t* x;
@@ -145,130 +158,176 @@ struct Stage1Args {
     ProxyView p;
     float* key;          // [B][f_pad]
     uint32_t* gh;        // [B][kGhBins] coarse key histogram (zero on entry)
+    double* part;        // [B][tiles + nb1][2][128] segment partial sums
+    unsigned long long* tcnt;   // [B][tiles] arrival counters: call tag << 32 | arrivals
     double* h_tap;       // [B][F] or null
     float* key_tap;      // [B][F] or null
     int32_t* in_idx_tap; // [B][k_in] or null
+    int tiles, nch, nb1;
+    uint32_t gen;        // tag of this call, distinct from earlier calls
 };
 
 constexpr int kS1Threads = 512;
 constexpr int kSlots = 64;
 constexpr int kChunk = 8;
 
-// Certain-or-all classification shared by both stages: with `all`, every
-// valid key is certain; otherwise the coarse digit decides.
-template <int P, int NT>
-__device__ __forceinline__ SelectState classify(const uint32_t (&key)[P], const bool (&valid)[P],
-                                                int k, bool all, int nbits, bool (&cert)[P],
-                                                int& cert_rank, uint32_t* hist, int* sc,
-                                                uint32_t* cand) {
-    if (all || k == 0) {
-        int nc = 0;
-#pragma unroll
-        for (int q = 0; q < P; ++q) {
-            cert[q] = all && valid[q];
-            nc += cert[q] ? 1 : 0;
-        }
-        int tot;
-        cert_rank = block_excl_scan<NT>(nc, sc, tot);
-        return SelectState{0u, 0, tot, k - tot, 0};
+// Items [i0, i1) of block w: i0 = w * T / nb1.  The block holding item i is the
+// largest w with i0(w) <= i.  The segment of (tile, block) is stored at
+// slot tile + block: along the tile-major item order both never decrease and
+// at least one grows, so the slots are distinct and below tiles + nb1.
+__device__ __host__ __forceinline__ long long s1_item0(int w, long long T, int nb1) { return (long long)w * T / nb1; }
+__device__ __host__ __forceinline__ int s1_block_of(long long i, long long T, int nb1) {
+    return (int)(((i + 1) * nb1 - 1) / T);
+}
+
+// Arrival at a split tile: the counter holds (call tag << 32 | arrivals); a
+// counter left by an earlier call (or never cleared) carries another tag and
+// restarts at 1.  Returns 1 for the arrival that completes the tile.
+__device__ __forceinline__ int s1_arrive(unsigned long long* cnt, uint32_t gen, int nseg) {
+    unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const unsigned long long nxt = (cur >> 32) == gen ? cur + 1 : (((unsigned long long)gen << 32) | 1ull);
+        if (__hip_atomic_compare_exchange_strong(cnt, &cur, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return (int)(nxt & 0xffffffffull) == nseg ? 1 : 0;
     }
-    return block_select_coarse<P, NT>(key, valid, k, nbits, cert, cert_rank, hist, sc, cand);
+}
+
+// h~ = silu(g~) u~ in fp64 (int8: per-channel scales applied here), the fp32
+// ranking key |h~| and its coarse histogram bin.
+__device__ __forceinline__ void stage1_score(const Stage1Args& a, int b, int j, double g, double u,
+                                             float sg, float su) {
+    if (j >= a.p.F) return;
+    if (a.p.kind == 1) {
+        g *= (double)sg;
+        u *= (double)su;
+    }
+    const double h = g / (1.0 + exp(-g)) * u;
+    const float kf = (float)fabs(h);
+    a.key[(size_t)b * a.p.f_pad + j] = kf;
+    __hip_atomic_fetch_add(a.gh + (size_t)b * kGhBins + (__float_as_uint(kf) >> kGhShift), 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.h_tap) a.h_tap[(size_t)b * a.p.F + j] = h;
+    if (a.key_tap) a.key_tap[(size_t)b * a.p.F + j] = kf;
 }
 
 // One chunk of <= 8 kept rows for one lane: the packed list entries and the
-// lane's 16-byte block of each tile row.
+// lane's 16-byte block of each tile row (buffer loads: tile offset scalar,
+// row and block offset per lane).  Entries past the segment or the list read
+// as x = 0 at an offset past the end of the codes, which the hardware returns
+// as zeros without a memory access; the loads are unconditional so they stay
+// in flight.
 struct Chunk {
     uint32_t e[kChunk];
     uint4 v[kChunk];
 };
 
-__device__ __forceinline__ void load_chunk(const uint32_t* list, int k_in, int ch, int nchunks,
-                                           const uint8_t* base, Chunk& c) {
+__device__ __forceinline__ void load_chunk(const uint32_t* list, int k_in, int ch, int ch_end,
+                                           __amdgpu_buffer_rsrc_t codes, uint32_t codes_bytes,
+                                           uint32_t tile_off, uint32_t lane_off, Chunk& c) {
     const int r0 = ch * kChunk;
-    const int n = ch < nchunks ? min(kChunk, k_in - r0) : 0;
+    const int n = ch < ch_end ? min(kChunk, k_in - r0) : 0;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-        if (u < n) {
-            c.e[u] = list[r0 + u];
-            c.v[u] = *reinterpret_cast<const uint4*>(base + (size_t)(c.e[u] >> 16) * kTileRowBytes);
-        } else {
-            c.e[u] = 0;                       // x = +0: contributes nothing
-            c.v[u] = make_uint4(0, 0, 0, 0);
-        }
+        const uint32_t e = list[u < n ? r0 + u : 0];
+        c.e[u] = u < n ? e : 0u;
+        const uint32_t off = u < n ? (e >> 16) * (uint32_t)kTileRowBytes + lane_off : codes_bytes;
+        c.v[u] = buf_load16(codes, off, tile_off);
     }
 }
 
-// Input selection of Stage 1.  The kept list holds (index << 16 | bf16 bits):
-// first the certain inputs in index order, then the kept candidates in index
-// order (the GEMV sums over the list, so only the set matters).  Then one
-// flag per chunk of 8 entries: 1 when the chunk's x exponents span at most
-// `spread_limit` binades (its products can be summed exactly in fp32).
-template <int PX>
-__device__ int stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32_t* cand,
-                             uint8_t* flags, uint32_t* hist, int* sc, int spread_limit) {
-    const int t = threadIdx.x;
-    const int k_in = a.k_in;
-    uint32_t raw[PX], key[PX];
-    bool valid[PX];
-    load_u16_contig<PX>(a.x + (size_t)b * a.d, a.d, a.d, raw, valid);
+// 1 when the chunk's nonzero x span at most 6 binades and none is subnormal.
+__device__ __forceinline__ bool chunk_exact32(const Chunk& c) {
+    int lo = 255, hi = 0;
+    bool ok = true;
 #pragma unroll
-    for (int q = 0; q < PX; ++q) key[q] = raw[q] & 0x7fffu;
-    const bool all = k_in >= a.d;
-    bool cert[PX];
-    int crank;
-    SelectState st = classify<PX, kS1Threads>(key, valid, k_in, all, 15, cert, crank, hist, sc, cand);
-    const int cbase = crank;   // certain keys before this thread's elements
-#pragma unroll
-    for (int q = 0; q < PX; ++q) {
-        if (cert[q]) list[crank] = ((uint32_t)(t * PX + q) << 16) | raw[q];
-        crank += cert[q] ? 1 : 0;
+    for (int u = 0; u < kChunk; ++u) {
+        const uint32_t r = c.e[u];
+        const int e = (int)((r >> 7) & 0xffu);
+        const bool zero = (r & 0x7fffu) == 0;       // +-0 contributes exactly 0
+        ok = ok && (zero || e != 0);                 // subnormal x: take the fp64 path
+        lo = zero ? lo : min(lo, e);
+        hi = zero ? hi : max(hi, e);
     }
-    // the candidates of the threshold bin (none when all or k_in == 0)
-    const int n_cert = st.above;
-    if (!all && k_in > 0) {
-        uint32_t T;
-        int cgt;
-        block_select_refine<kS1Threads>(st, cand, T, cgt, hist, sc);
-        bool on[PX];
-        int pos[PX];
-        block_keep_and_rank<PX, kS1Threads>(key, valid, false, k_in, T, cgt, on, pos, sc);
-        int cb = 0;     // certain keys of this thread before element q
+    return ok && hi - lo <= 6;
+}
+
+// Input selection.  Fills `list` with the k_in kept inputs in index order.
+// Keys are 15 bits: a 2048-bin histogram of key >> 4 finds the threshold bin,
+// a 16-bin histogram of the low 4 bits of the keys in that bin finds the
+// threshold T itself (every thread scans those 16 bins), and one packed scan
+// of (keys > T, keys == T) places every kept input, the first k_in - #(> T)
+// keys equal to T in index order.  LDS: hist >= 2048 + 16 + 64 words.
+template <int PX>
+__device__ void stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32_t* hist, int* sc) {
+    constexpr int NT = kS1Threads;
+    const int t = threadIdx.x, lane = t & 63;
+    const int d = a.d, k_in = a.k_in;
+    uint32_t raw[PX];
+    int key[PX];
+    {
+        bool valid[PX];
+        load_u16_contig<PX>(a.x + (size_t)b * d, d, d, raw, valid);
 #pragma unroll
-        for (int q = 0; q < PX; ++q) {
-            const int j = t * PX + q;
-            if (on[q] && !cert[q]) list[n_cert + pos[q] - (cbase + cb)] = ((uint32_t)j << 16) | raw[q];
-            if (on[q] && a.in_idx_tap && blockIdx.x == 0) a.in_idx_tap[(size_t)b * k_in + pos[q]] = j;
-            cb += cert[q] ? 1 : 0;
-        }
-    } else if (all && a.in_idx_tap && blockIdx.x == 0) {
+        for (int q = 0; q < PX; ++q) key[q] = valid[q] ? (int)(raw[q] & 0x7fffu) : -1;   // past d: below every key
+    }
+    const bool all = k_in >= d;
+    int T = -1, cgt = 0;                                   // keep-all: every valid key is above T
+    if (!all && k_in > 0) {
+        uint32_t* hist2 = hist + 2048;
+        for (int i = t; i < 2048 + 16; i += NT) hist[i] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < PX; ++q) atomicAdd(&hist[key[q] >= 0 ? (key[q] >> 4) : 2048 + 16], 1u);
+        lds_barrier();
+        uint32_t tb;
+        find_bin<NT>(hist, 2048, k_in, sc, tb, cgt);
 #pragma unroll
         for (int q = 0; q < PX; ++q)
-            if (cert[q]) a.in_idx_tap[(size_t)b * k_in + t * PX + q] = t * PX + q;
-    }
-    lds_barrier();
-    const int nchunks = (k_in + kChunk - 1) / kChunk;
-    for (int c = t; c < nchunks; c += kS1Threads) {
-        int lo = 255, hi = 0;
-        bool ok = true;
-        const int n = min(kChunk, k_in - c * kChunk);
-        for (int u = 0; u < n; ++u) {
-            const uint32_t r = list[c * kChunk + u];
-            const int e = (int)((r >> 7) & 0xffu);
-            if ((r & 0x7fffu) == 0) continue;   // +-0 contributes exactly 0
-            if (e == 0) ok = false;              // subnormal x: take the fp64 path
-            lo = min(lo, e);
-            hi = max(hi, e);
+            if (key[q] >= 0 && (key[q] >> 4) == (int)tb) atomicAdd(&hist2[key[q] & 15], 1u);
+        lds_barrier();
+        int cum = cgt;
+        T = (int)(tb << 4);
+        for (int v = 15; v >= 0; --v) {                    // every thread: same answer
+            const int c = (int)hist2[v];
+            if (cum + c >= k_in) {
+                T = (int)(tb << 4) + v;
+                break;
+            }
+            cum += c;
         }
-        flags[c] = (ok && hi - lo <= spread_limit) ? 1 : 0;
+        cgt = cum;                                         // keys > T
+    }
+    const int need = all ? 0 : k_in - cgt;                 // keys equal to T to keep
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int q = 0; q < PX; ++q) {
+        gt += key[q] > T ? 1 : 0;
+        eq += (key[q] == T && !all) ? 1 : 0;
+    }
+    int tot;
+    // fewer than k_in <= 2^15 keys exceed T (keep-all: at most d keys, unpacked)
+    const uint32_t pre = (uint32_t)block_excl_scan<NT>(all ? gt : (int)(((uint32_t)gt << 16) | (uint32_t)eq), sc, tot);
+    if (k_in > 0) {
+        int eb = all ? 0 : (int)(pre & 0xffffu);
+        int pos = all ? (int)pre : (int)(pre >> 16) + min(eb, need);
+        uint32_t* dummy = list + k_in + lane;              // lanes with nothing to write
+#pragma unroll
+        for (int q = 0; q < PX; ++q) {
+            const bool e = key[q] == T && !all;
+            const bool on = key[q] > T || (e && eb < need);
+            *(on ? list + pos : dummy) = ((uint32_t)(t * PX + q) << 16) | raw[q];
+            if (on && a.in_idx_tap && blockIdx.x == 0) a.in_idx_tap[(size_t)b * k_in + pos] = t * PX + q;
+            eb += e ? 1 : 0;
+            pos += on ? 1 : 0;
+        }
     }
     lds_barrier();
-    return nchunks;
 }
 
 // int8 chunk: 8 gate + 8 up channels of the lane.
-__device__ __forceinline__ void consume_chunk_i8(const Chunk& c, bool exact32, double (&ag)[8],
-                                                 double (&au)[8]) {
-    if (exact32) {
+__device__ __forceinline__ void consume_chunk_i8(const Chunk& c, double (&ag)[8], double (&au)[8]) {
+    if (chunk_exact32(c)) {
         float sg[8], su[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) sg[q] = su[q] = 0.f;
@@ -305,83 +364,103 @@ __device__ __forceinline__ void consume_chunk_i8(const Chunk& c, bool exact32, d
 
 // int4 chunk: 16 gate + 16 up channels of the lane; the inner sums of a
 // 128-input group are scaled into og/ou when the row's group changes.
-__device__ __forceinline__ void consume_chunk_i4(const Chunk& c, int n, const float* sgp,
-                                                 const float* sup, int f_pad, int& cur,
-                                                 double (&ag)[16], double (&au)[16],
+__device__ __forceinline__ void consume_chunk_i4(const Chunk& c, const float* sgp, const float* sup,
+                                                 int f_pad, int& cur, double (&ag)[16], double (&au)[16],
                                                  double (&og)[16], double (&ou)[16]) {
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-        if (u < n) {
-            const int g = (int)(c.e[u] >> 16) >> 7;
-            if (g != cur) {
-                if (cur >= 0) {
-                    const float4* s4g = reinterpret_cast<const float4*>(sgp + (size_t)cur * f_pad);
-                    const float4* s4u = reinterpret_cast<const float4*>(sup + (size_t)cur * f_pad);
+        const int g = (int)(c.e[u] >> 16) >> 7;
+        if (g != cur) {
+            if (cur >= 0) {
+                const float4* s4g = reinterpret_cast<const float4*>(sgp + (size_t)cur * f_pad);
+                const float4* s4u = reinterpret_cast<const float4*>(sup + (size_t)cur * f_pad);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 fg = s4g[q], fu = s4u[q];
-                        og[4 * q + 0] = fma(ag[4 * q + 0], (double)fg.x, og[4 * q + 0]);
-                        og[4 * q + 1] = fma(ag[4 * q + 1], (double)fg.y, og[4 * q + 1]);
-                        og[4 * q + 2] = fma(ag[4 * q + 2], (double)fg.z, og[4 * q + 2]);
-                        og[4 * q + 3] = fma(ag[4 * q + 3], (double)fg.w, og[4 * q + 3]);
-                        ou[4 * q + 0] = fma(au[4 * q + 0], (double)fu.x, ou[4 * q + 0]);
-                        ou[4 * q + 1] = fma(au[4 * q + 1], (double)fu.y, ou[4 * q + 1]);
-                        ou[4 * q + 2] = fma(au[4 * q + 2], (double)fu.z, ou[4 * q + 2]);
-                        ou[4 * q + 3] = fma(au[4 * q + 3], (double)fu.w, ou[4 * q + 3]);
-                    }
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) ag[q] = au[q] = 0.0;
+                for (int q = 0; q < 4; ++q) {
+                    const float4 fg = s4g[q], fu = s4u[q];
+                    og[4 * q + 0] = fma(ag[4 * q + 0], (double)fg.x, og[4 * q + 0]);
+                    og[4 * q + 1] = fma(ag[4 * q + 1], (double)fg.y, og[4 * q + 1]);
+                    og[4 * q + 2] = fma(ag[4 * q + 2], (double)fg.z, og[4 * q + 2]);
+                    og[4 * q + 3] = fma(ag[4 * q + 3], (double)fg.w, og[4 * q + 3]);
+                    ou[4 * q + 0] = fma(au[4 * q + 0], (double)fu.x, ou[4 * q + 0]);
+                    ou[4 * q + 1] = fma(au[4 * q + 1], (double)fu.y, ou[4 * q + 1]);
+                    ou[4 * q + 2] = fma(au[4 * q + 2], (double)fu.z, ou[4 * q + 2]);
+                    ou[4 * q + 3] = fma(au[4 * q + 3], (double)fu.w, ou[4 * q + 3]);
                 }
-                cur = g;
-            }
-            const double xd = (double)bf16f(c.e[u] & 0xffffu);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                ag[q] = fma(xd, (double)sext4(c.v[u].x, q), ag[q]);
-                ag[q + 8] = fma(xd, (double)sext4(c.v[u].y, q), ag[q + 8]);
-                au[q] = fma(xd, (double)sext4(c.v[u].z, q), au[q]);
-                au[q + 8] = fma(xd, (double)sext4(c.v[u].w, q), au[q + 8]);
+                for (int q = 0; q < 16; ++q) ag[q] = au[q] = 0.0;
             }
+            cur = g;
+        }
+        const double xd = (double)bf16f(c.e[u] & 0xffffu);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            ag[q] = fma(xd, (double)sext4(c.v[u].x, q), ag[q]);
+            ag[q + 8] = fma(xd, (double)sext4(c.v[u].y, q), ag[q + 8]);
+            au[q] = fma(xd, (double)sext4(c.v[u].z, q), au[q]);
+            au[q + 8] = fma(xd, (double)sext4(c.v[u].w, q), au[q + 8]);
         }
     }
 }
 
+template <int N>
+__device__ __forceinline__ void settle_d(double (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]) : : "memory");
+}
+
 template <int KIND, int PX>
-__global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) {
+__global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     constexpr int TC = KIND == 1 ? 64 : 128;            // channels per tile
     constexpr int NV = KIND == 1 ? 8 : 16;               // channels per lane
+    constexpr int NW = kS1Threads / kWave;
     extern __shared__ uint32_t dyn[];
-    __shared__ uint32_t hist[2048 + 64];
+    __shared__ uint32_t hist[2048 + 16 + 64];
     __shared__ int sc[24];
     __shared__ double red[8][2][TC];
+    __shared__ double gsum[2][TC];
 
-    const int b = blockIdx.y;
+    const int b = blockIdx.y, wb = blockIdx.x;
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
-    const int k_in = a.k_in, d = a.d;
-    uint32_t* list = dyn;                         // [k_in]
-    uint32_t* cand = dyn + k_in;                  // [d + 64]
-    uint8_t* flags = reinterpret_cast<uint8_t*>(dyn + k_in + d + 64);
-    const int nchunks = stage1_select<PX>(a, b, list, cand, flags, hist, sc, 6);
+    const int k_in = a.k_in, d = a.d, nch = a.nch;
+    uint32_t* list = dyn;                         // [k_in + 64]
+    stage1_select<PX>(a, b, list, hist, sc);
 
+    const long long T = (long long)a.tiles * nch;
+    const long long i0 = s1_item0(wb, T, a.nb1), i1 = s1_item0(wb + 1, T, a.nb1);
     const int slot = w * 8 + (l >> 3);
     const int cb = l & 7;
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-        const uint8_t* base = a.p.codes + (size_t)tile * d * kTileRowBytes + cb * 16;
+    const uint32_t codes_bytes = (uint32_t)a.tiles * (uint32_t)d * (uint32_t)kTileRowBytes;
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.p.codes, codes_bytes);
+    const uint32_t lane_off = (uint32_t)cb * 16u;
+    for (int tile = (int)(i0 / nch); (long long)tile * nch < i1; ++tile) {
+        const int ca = (int)(max(i0, (long long)tile * nch) - (long long)tile * nch);
+        const int ce = (int)(min(i1, (long long)(tile + 1) * nch) - (long long)tile * nch);
+        const uint32_t tile_off = (uint32_t)tile * (uint32_t)d * (uint32_t)kTileRowBytes;
+        // int8 channel scales, requested now and used after the stream
+        float sgj = 0.f, suj = 0.f;
+        if constexpr (KIND == 1) {
+            const int j = tile * TC + (t % TC);             // < f_pad: always readable
+            sgj = a.p.scales[j];
+            suj = a.p.scales[(size_t)a.p.f_pad + j];
+        }
         double ag[NV], au[NV];
 #pragma unroll
         for (int c = 0; c < NV; ++c) ag[c] = au[c] = 0.0;
 
-        // chunks slot, slot + 64, ...: the next chunk's rows are in flight while
-        // the current one is accumulated
+        // chunks ca + slot, + 64, ...: two chunks in flight per slot; the loop
+        // has no exit from its middle and its loads are unconditional
         Chunk c0, c1;
         if constexpr (KIND == 1) {
-            load_chunk(list, k_in, slot, nchunks, base, c0);
-            for (int ch = slot; ch < nchunks; ch += 2 * kSlots) {
-                load_chunk(list, k_in, ch + kSlots, nchunks, base, c1);
-                consume_chunk_i8(c0, flags[ch] != 0, ag, au);
-                if (ch + kSlots >= nchunks) break;
-                load_chunk(list, k_in, ch + 2 * kSlots, nchunks, base, c0);
-                consume_chunk_i8(c1, flags[ch + kSlots] != 0, ag, au);
+            load_chunk(list, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
+            for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
+                load_chunk(list, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
+                consume_chunk_i8(c0, ag, au);
+                settle_d(ag);
+                settle_d(au);
+                load_chunk(list, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
+                consume_chunk_i8(c1, ag, au);
+                settle_d(ag);
+                settle_d(au);
             }
         } else {
             const float* sgp = a.p.scales + (size_t)tile * TC + cb * 16;
@@ -390,13 +469,14 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) 
 #pragma unroll
             for (int c = 0; c < NV; ++c) og[c] = ou[c] = 0.0;
             int cur = -1;
-            load_chunk(list, k_in, slot, nchunks, base, c0);
-            for (int ch = slot; ch < nchunks; ch += 2 * kSlots) {
-                load_chunk(list, k_in, ch + kSlots, nchunks, base, c1);
-                consume_chunk_i4(c0, min(kChunk, k_in - ch * kChunk), sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
-                if (ch + kSlots >= nchunks) break;
-                load_chunk(list, k_in, ch + 2 * kSlots, nchunks, base, c0);
-                consume_chunk_i4(c1, min(kChunk, k_in - (ch + kSlots) * kChunk), sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
+            load_chunk(list, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
+            for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
+                load_chunk(list, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
+                consume_chunk_i4(c0, sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
+                settle_d(og);
+                load_chunk(list, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
+                consume_chunk_i4(c1, sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
+                settle_d(og);
             }
             if (cur >= 0) {
                 const float* sg = sgp + (size_t)cur * a.p.f_pad;
@@ -430,64 +510,74 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a, int tiles) 
             }
         }
         lds_barrier();
-        if (t < TC) {
-            const int j = tile * TC + t;
-            if (j < a.p.F) {
-                double g = 0.0, u = 0.0;
+        // this segment's sums: thread t < 2 TC holds channel t % TC, gate (t < TC) or up
+        double v = 0.0;
+        if (t < 2 * TC) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    g += red[q][0][t];
-                    u += red[q][1][t];
-                }
-                if (KIND == 1) {
-                    g *= (double)a.p.scales[j];
-                    u *= (double)a.p.scales[(size_t)a.p.f_pad + j];
-                }
-                const double h = g / (1.0 + exp(-g)) * u;
-                const float kf = (float)fabs(h);
-                a.key[(size_t)b * a.p.f_pad + j] = kf;
-                __hip_atomic_fetch_add(a.gh + (size_t)b * kGhBins + (__float_as_uint(kf) >> kGhShift), 1u,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (a.h_tap) a.h_tap[(size_t)b * a.p.F + j] = h;
-                if (a.key_tap) a.key_tap[(size_t)b * a.p.F + j] = kf;
+            for (int q = 0; q < 8; ++q) v += red[q][t / TC][t % TC];
+        }
+        const int w0 = s1_block_of((long long)tile * nch, T, a.nb1);
+        const int w1 = s1_block_of((long long)(tile + 1) * nch - 1, T, a.nb1);
+        bool last = true;
+        if (w1 > w0) {
+            // the tile is split: publish this segment, and the block that
+            // completes the tile adds the segments in block order
+            // (device-scope stores and loads: they are coherent across the
+            // chip's L2 caches without writing back or invalidating whole
+            // caches; the stores have completed before the arrival is counted)
+            double* slot = a.part + ((size_t)b * (a.tiles + a.nb1) + tile) * 2 * kPartChannels;
+            if (t < 2 * TC)
+                __hip_atomic_store(&slot[((size_t)2 * wb + t / TC) * kPartChannels + t % TC], v,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            if (t == 0) sc[22] = s1_arrive(a.tcnt + (size_t)b * a.tiles + tile, a.gen, w1 - w0 + 1);
+            lds_barrier();
+            last = sc[22] != 0;
+            if (last && t < 2 * TC) {
+                v = 0.0;
+                for (int w = w0; w <= w1; ++w)
+                    v += __hip_atomic_load(&slot[((size_t)2 * w + t / TC) * kPartChannels + t % TC],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        lds_barrier();   // `red` is rewritten by the next tile
+        if (last) {
+            if (t < 2 * TC) gsum[t / TC][t % TC] = v;
+            lds_barrier();
+            if (t < TC) stage1_score(a, b, tile * TC + t, gsum[0][t], gsum[1][t], sgj, suj);
+        }
+        lds_barrier();   // `red` and `gsum` are rewritten by the next tile
     }
 }
 
 template <int KIND, int PX>
-static hipError_t go_stage1(const Stage1Args& a, int B, int n_cu, hipStream_t s) {
-    const int tiles = a.p.f_pad / (KIND == 1 ? 64 : 128);
-    const size_t dyn = (size_t)(a.k_in + a.d + 64) * 4 + (a.k_in + kChunk - 1) / kChunk + 16;
+static hipError_t go_stage1(const Stage1Args& a, int B, hipStream_t s) {
+    const size_t dyn = (size_t)(a.k_in + 64) * 4;
     auto fn = k_stage1<KIND, PX>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    // one block per compute unit over the batch; each block loops over tiles
-    int gx = n_cu / B;
-    if (gx < 1) gx = 1;
-    if (gx > tiles) gx = tiles;
-    hipLaunchKernelGGL(fn, dim3(gx, B), dim3(kS1Threads), dyn, s, a, tiles);
+    hipLaunchKernelGGL(fn, dim3(a.nb1, B), dim3(kS1Threads), dyn, s, a);
     return hipGetLastError();
 }
 
 template <int KIND>
-static hipError_t stage1_px(const Stage1Args& a, int B, int n_cu, hipStream_t s) {
+static hipError_t stage1_px(const Stage1Args& a, int B, hipStream_t s) {
     const int per = (a.d + kS1Threads - 1) / kS1Threads;
-    if (per <= 8) return go_stage1<KIND, 8>(a, B, n_cu, s);
-    if (per <= 16) return go_stage1<KIND, 16>(a, B, n_cu, s);
-    if (per <= 24) return go_stage1<KIND, 24>(a, B, n_cu, s);
-    return go_stage1<KIND, 32>(a, B, n_cu, s);
+    if (per <= 8) return go_stage1<KIND, 8>(a, B, s);
+    if (per <= 16) return go_stage1<KIND, 16>(a, B, s);
+    if (per <= 24) return go_stage1<KIND, 24>(a, B, s);
+    return go_stage1<KIND, 32>(a, B, s);
 }
 
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
-                         uint32_t* gh, double* h_tap, float* key_tap, int32_t* in_idx_tap, int n_cu,
+                         uint32_t* gh, double* part, unsigned long long* tcnt, uint32_t gen,
+                         const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
                          hipStream_t s) {
-    Stage1Args a{x, d, k_in, p, key, gh, h_tap, key_tap, in_idx_tap};
-    return p.kind == 1 ? stage1_px<1>(a, B, n_cu, s) : stage1_px<2>(a, B, n_cu, s);
+    Stage1Args a{x, d, k_in, p, key, gh, part, tcnt, h_tap, key_tap, in_idx_tap, g.tiles, g.nch, g.nb1, gen};
+    return p.kind == 1 ? stage1_px<1>(a, B, s) : stage1_px<2>(a, B, s);
 }
+
 
 // ---------------------------------------------------------------------------
 // Stage 2.  grid (W2, B), block 512 (8 waves).  Block w of token b owns the
@@ -523,25 +613,27 @@ struct RowGroup {
 
 // Rows of list entries v0 .. v0 + G - 1 (buffer loads: the row offset is
 // scalar, the column offset `voff` is this thread's).  Loads are unconditional
-// so the compiler keeps them in flight: entries past `last` re-read entry
-// `last` (in cache; their h is zeroed), columns past d re-read column 0 (x is 0
-// there).
+// so the compiler keeps them in flight: entries at or past `cnt` (their h is
+// zeroed) and columns past d (x is 0 there) read at an offset past the end of
+// the matrix, which the hardware returns as zeros without a memory access.
 struct RowRsrc {
     __amdgpu_buffer_rsrc_t g, u, dn;
 };
 
 template <int R, int G>
-__device__ __forceinline__ void load_group(const RowRsrc& rs, const uint16_t* chan, int v0, int last,
-                                           uint32_t row_bytes, const uint32_t (&voff)[R],
+__device__ __forceinline__ void load_group(const RowRsrc& rs, const uint16_t* chan, int v0, int cnt,
+                                           uint32_t row_bytes, uint32_t oob, const uint32_t (&voff)[R],
                                            RowGroup<R, G>& rg) {
 #pragma unroll
     for (int q = 0; q < G; ++q) {
-        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)chan[min(v0 + q, last)]) * row_bytes;
+        const bool ok = v0 + q < cnt;
+        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)chan[min(v0 + q, max(cnt - 1, 0))]) * row_bytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            rg.g[q][r] = buf_load16(rs.g, voff[r], soff);
-            rg.u[q][r] = buf_load16(rs.u, voff[r], soff);
-            rg.dn[q][r] = buf_load16(rs.dn, voff[r], soff);
+            const uint32_t vo = ok ? voff[r] : oob;
+            rg.g[q][r] = buf_load16(rs.g, vo, soff);
+            rg.u[q][r] = buf_load16(rs.u, vo, soff);
+            rg.dn[q][r] = buf_load16(rs.dn, vo, soff);
         }
     }
 }
@@ -634,36 +726,6 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
 // ---------------------------------------------------------------------------
 constexpr int kSmallCand = 128;   // candidates ranked by direct comparison up to this many
 
-// Per-wave ballot counts of up to 4 predicates, then the block-wide exclusive
-// positions and totals.  `wc` = [4][8] ints of LDS; ends with a barrier that
-// makes `wc` reusable.
-template <int NP>
-__device__ __forceinline__ void block_ballot_pos(const bool (&p)[NP], int (*wc)[kS2Threads / kWave],
-                                                 int (&pos)[NP], int (&tot)[NP]) {
-    constexpr int NW = kS2Threads / kWave;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    uint64_t m[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        m[i] = __ballot(p[i]);
-        if (lane == 0) wc[i][wv] = __popcll(m[i]);
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        int off = 0, all = 0;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-            const int c = wc[i][v];
-            all += c;
-            off += v < wv ? c : 0;
-        }
-        pos[i] = off + lanes_below(m[i]);
-        tot[i] = all;
-    }
-    lds_barrier();
-}
-
 template <int PK, int R, int G>
 __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     constexpr int NT = kS2Threads;
@@ -690,7 +752,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int col = r * 4096 + t * 8;
-        voff[r] = col < a.d ? (uint32_t)col * 2u : 0u;
+        voff[r] = col < a.d ? (uint32_t)col * 2u : mat_bytes;   // past d: read as zeros
         uint4 v = make_uint4(0, 0, 0, 0);
         if (col < a.d) v = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
         xr[r][0] = bf16_lo(v.x); xr[r][1] = bf16_hi(v.x);
@@ -780,7 +842,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int cert_before = sc[18];                        // certain keys before the range
     const int E = min(nc, G);
     RowGroup<R, G> cur, nxt;
-    load_group<R, G>(rs, chan, 0, max(E - 1, 0), row_bytes, voff, cur);
+    load_group<R, G>(rs, chan, 0, E, row_bytes, mat_bytes, voff, cur);
 
     // ---- resolve the candidates while those loads are in flight: cand[i]
     // gets bit 31 when kept
@@ -813,7 +875,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
                 const uint32_t v = i < ncand ? cand[i] : 0u;
                 bool p[1] = {i < ncand && v == T};
                 int pos[1], tt[1];
-                block_ballot_pos<1>(p, wc, pos, tt);
+                block_ballot_pos<kS2Threads, 1>(p, wc, pos, tt);
                 if (i < ncand && (v > T || (p[0] && eq_run + pos[0] < eq_need))) cand[i] = v | 0x80000000u;
                 eq_run += tt[0];
             }
@@ -830,7 +892,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             const bool kept = i < ncand && (cand[i] >> 31) != 0;
             bool p[2] = {kept, kept && i < cs};
             int pos[2], tt[2];
-            block_ballot_pos<2>(p, wc, pos, tt);
+            block_ballot_pos<kS2Threads, 2>(p, wc, pos, tt);
             pos[0] += run;
             run += tt[0];
             kc_before += tt[1];
@@ -865,11 +927,11 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             const uint32_t v = c0r == 0 ? own0 : (in ? __float_as_uint(keyb[j]) : 0u);
             bool p1[1] = {in && is_cand(v)};
             int pos1[1], t1[1];
-            block_ballot_pos<1>(p1, wc, pos1, t1);
+            block_ballot_pos<kS2Threads, 1>(p1, wc, pos1, t1);
             const bool kc = p1[0] && (cand[cs + nd_run + pos1[0]] >> 31) != 0;
             bool p2[1] = {in && (is_cert(v) || kc)};
             int pos2[1], t2[1];
-            block_ballot_pos<1>(p2, wc, pos2, t2);
+            block_ballot_pos<kS2Threads, 1>(p2, wc, pos2, t2);
             if (p2[0] && a.idx) a.idx[(size_t)b * k + kept_before + nk + pos2[0]] = j;
             if (in && a.mask) a.mask[(size_t)b * F + j] = p2[0] ? 1 : 0;
             nd_run += t1[0];
@@ -883,20 +945,19 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     // ---- sparse SwiGLU: group 0 = entries [0, E), then [E, n) G at a time.
     // The loads are unconditional and the loop has no exit from its middle:
     // on any path that merges pending and completed loads the compiler drains
-    // every load and the overlap is lost.  After the last group, `cur` re-reads
-    // the last entry (cache hits) and is left unused.
+    // every load and the overlap is lost.  After the last group, `cur` is
+    // loaded past the list (zeros, no memory access) and left unused.
     const int rest = n - E;
     const int groups = 1 + (rest + G - 1) / G;
-    const int last = max(n - 1, 0);
     int gi = 0;
     for (; gi + 1 < groups; gi += 2) {
-        load_group<R, G>(rs, chan, E + gi * G, last, row_bytes, voff, nxt);
+        load_group<R, G>(rs, chan, E + gi * G, n, row_bytes, mat_bytes, voff, nxt);
         consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
         // The accumulation into y must finish before `cur` is reloaded: if the
         // compiler sinks it below the reloads, the old and new `cur` overlap
         // and the loop-carried registers need a copy that waits for the loads.
         settle(yacc);
-        load_group<R, G>(rs, chan, E + (gi + 1) * G, last, row_bytes, voff, cur);
+        load_group<R, G>(rs, chan, E + (gi + 1) * G, n, row_bytes, mat_bytes, voff, cur);
         consume_group<R, G>(nxt, xr, yacc, min(G, rest - gi * G), red[1]);
         settle(yacc);
     }
