@@ -56,7 +56,13 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, --steps times (the reference "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args(argv)
+
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -156,7 +162,7 @@ def main(argv=None):
     # dominant kernel: the phase with the largest share of the step
     dom = int(np.argmax(phase_ms))
     dom_name = P.PHASES[dom]
-    dom_bytes = {1: proxy_b, 4: stage2_b}.get(dom, total_b)
+    dom_bytes = {0: proxy_b, 1: stage2_b}.get(dom, total_b)
     dom_gbs = dom_bytes / (phase_ms[dom] * 1e-3) / 1e9
 
     out = {
@@ -191,6 +197,30 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, layer, w, xs, k_in, k_ff, total_b / B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def copy_calibration(mib, steps):
+    """A plain device-to-device copy of known size: it reads and writes exactly
+    mib MiB per launch, so hardware byte counters read on it give the factor
+    between what they report and the bytes moved."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": steps + 3,
+                      "us_per_copy": round(ms * 1e3, 2), "GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
     return 0
 
 
