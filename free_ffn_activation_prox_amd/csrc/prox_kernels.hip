@@ -127,30 +127,26 @@ hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d,
 // Stage 1.  grid (NB1, B), block 512 (8 waves).
 //
 // Work items: (tile, chunk) pairs, tile-major, chunk = 8 consecutive entries
-// of the token's kept-input list; block w takes items [w*T/NB1, (w+1)*T/NB1)
+// of the token's kept-input list.  int8 with no more tiles than blocks: one
+// whole tile per block.  Otherwise block w takes items [w*T/NB1, (w+1)*T/NB1)
 // of the T = tiles * nch items, so every compute unit streams the same number
-// of proxy rows whatever the tile count.  A block's share of a tile is a
-// "segment"; its partial gate/up sums go to `part` and the score kernel adds
-// the segments of each tile in segment order.
+// of proxy rows whatever the tile count; a tile split between blocks has its
+// segment sums added, in block order, by the block that completes it.
 //
 // Input selection: thread t holds x[t*PX .. t*PX + PX - 1]; keys are the 15
-// magnitude bits of the bf16 value (monotone in |x|, -0 == +0).  Keys in bins
-// (key >> 4) above the threshold bin are kept for certain; the candidates of
-// that bin are ranked (key descending, index ascending) by direct comparison.
-// The list in LDS holds (index << 16 | bf16 bits): the certain inputs in index
-// order, then the kept candidates in index order (the GEMV sums over the list,
-// so only the set matters).
+// magnitude bits of the bf16 value (monotone in |x|, -0 == +0).  The list in
+// LDS holds (index << 16 | bf16 bits) of the kept inputs: first those whose
+// exponent is at most 5 above the threshold's, then the larger ones, each in
+// index order (the GEMV sums over the list, so only the set matters).
 //
 // GEMV: row slot s (= 8 * wave + lane / 8, 64 slots) takes the segment's chunks
 // s, s + 64, ...; lane % 8 picks a 16-byte block of the tile row (int8: 8 gate
-// + 8 up codes; int4: 16 + 16).  int8 chunks accumulate in fp32 when the
-// chunk's x exponents span <= 6 binades: every product x * q is then a multiple
-// of 2^(e_lo - 7) below 2^(e_hi + 8), so the partial sums of <= 8 products are
-// integers below 2^24 in those units and every fp32 step is exact; the chunk
-// sum is then added to the fp64 accumulator.  Other chunks accumulate in fp64
-// directly.  int4 accumulates in fp64 and scales each 128-input group's inner
-// sum when the group changes.  The slots are reduced with lane shuffles and
-// LDS in a fixed order, so the result is deterministic.
+// + 8 up codes; int4: 16 + 16).  int8 chunks whose x span at most 5 binades
+// accumulate exactly in fp32 (see consume_chunk_i8) and the chunk sum is added
+// to the fp64 accumulator; other chunks accumulate in fp64 directly.  int4
+// accumulates in fp64 and scales each 128-input group's inner sum when the
+// group changes.  The slots are reduced with lane shuffles and LDS in a fixed
+// order, so the result is deterministic.
 // ---------------------------------------------------------------------------
 struct Stage1Args {
     const uint16_t* x;
@@ -236,7 +232,7 @@ __device__ __forceinline__ void load_chunk(const uint32_t* list, int k_in, int c
     }
 }
 
-// 1 when the chunk's nonzero x span at most 6 binades and none is subnormal.
+// 1 when the chunk's nonzero x span at most 5 binades and none is subnormal.
 __device__ __forceinline__ bool chunk_exact32(const Chunk& c) {
     int lo = 255, hi = 0;
     bool ok = true;
@@ -249,7 +245,7 @@ __device__ __forceinline__ bool chunk_exact32(const Chunk& c) {
         lo = zero ? lo : min(lo, e);
         hi = zero ? hi : max(hi, e);
     }
-    return ok && hi - lo <= 6;
+    return ok && hi - lo <= 5;
 }
 
 // Input selection.  Fills `list` with the k_in kept inputs in index order.
@@ -308,44 +304,81 @@ __device__ void stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32
     int tot;
     // fewer than k_in <= 2^15 keys exceed T (keep-all: at most d keys, unpacked)
     const uint32_t pre = (uint32_t)block_excl_scan<NT>(all ? gt : (int)(((uint32_t)gt << 16) | (uint32_t)eq), sc, tot);
-    if (k_in > 0) {
+    // Which keys are kept, and the list order.  The kept inputs whose
+    // exponent is at most 5 above the threshold's ("band B") come first, the
+    // larger ones after, each part in index order: chunks of band B span at
+    // most 5 binades, so they take the exact fp32 path, and a few large
+    // outlier inputs cannot push whole chunks onto the fp64 path.
+    bool on[PX];
+    {
         int eb = all ? 0 : (int)(pre & 0xffffu);
         int pos = all ? (int)pre : (int)(pre >> 16) + min(eb, need);
-        uint32_t* dummy = list + k_in + lane;              // lanes with nothing to write
 #pragma unroll
         for (int q = 0; q < PX; ++q) {
             const bool e = key[q] == T && !all;
-            const bool on = key[q] > T || (e && eb < need);
-            *(on ? list + pos : dummy) = ((uint32_t)(t * PX + q) << 16) | raw[q];
-            if (on && a.in_idx_tap && blockIdx.x == 0) a.in_idx_tap[(size_t)b * k_in + pos] = t * PX + q;
+            on[q] = k_in > 0 && (key[q] > T || (e && eb < need));
+            if (on[q] && a.in_idx_tap && blockIdx.x == 0) a.in_idx_tap[(size_t)b * k_in + pos] = t * PX + q;
             eb += e ? 1 : 0;
-            pos += on ? 1 : 0;
+            pos += on[q] ? 1 : 0;
+        }
+    }
+    const int e_hi = all ? 255 : ((T >> 7) & 0xff) + 5;    // keep-all: one band
+    int nb = 0, na = 0;
+#pragma unroll
+    for (int q = 0; q < PX; ++q) {
+        const bool big = ((key[q] >> 7) & 0xff) > e_hi;
+        nb += on[q] && !big ? 1 : 0;
+        na += on[q] && big ? 1 : 0;
+    }
+    int tot2;
+    const uint32_t pre2 = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)nb << 16) | (uint32_t)na), sc, tot2);
+    if (k_in > 0) {
+        int pb = (int)(pre2 >> 16), pa = (int)((uint32_t)tot2 >> 16) + (int)(pre2 & 0xffffu);
+        uint32_t* dummy = list + k_in + lane;              // lanes with nothing to write
+#pragma unroll
+        for (int q = 0; q < PX; ++q) {
+            const bool big = ((key[q] >> 7) & 0xff) > e_hi;
+            *(on[q] ? list + (big ? pa : pb) : dummy) = ((uint32_t)(t * PX + q) << 16) | raw[q];
+            pb += on[q] && !big ? 1 : 0;
+            pa += on[q] && big ? 1 : 0;
         }
     }
     lds_barrier();
 }
 
-// int8 chunk: 8 gate + 8 up channels of the lane.
+// Unsigned byte c of w as float (one conversion instruction).
+__device__ __forceinline__ float ubyte_f(uint32_t w, int c) { return (float)((w >> (8 * c)) & 0xffu); }
+
+// int8 chunk: 8 gate + 8 up channels of the lane.  Exact fp32 path: with the
+// code bytes flipped by 0x80 each byte reads as q + 128 in [1, 255], so
+// sum x*q = sum x*(q + 128) - 128 * sum x.  When the chunk's x span at most 5
+// binades every x is an integer below 2^13 in units of 2^(e_lo - 7), every
+// product below 2^21 and every partial sum below 2^24: all steps are exact,
+// and so is the final difference (its value is the exact sum x*q).
 __device__ __forceinline__ void consume_chunk_i8(const Chunk& c, double (&ag)[8], double (&au)[8]) {
     if (chunk_exact32(c)) {
-        float sg[8], su[8];
+        float sg[8], su[8], sx = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) sg[q] = su[q] = 0.f;
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
             const float xf = bf16f(c.e[u] & 0xffffu);
+            sx += xf;
+            const uint32_t gx = c.v[u].x ^ 0x80808080u, gy = c.v[u].y ^ 0x80808080u;
+            const uint32_t ux = c.v[u].z ^ 0x80808080u, uy = c.v[u].w ^ 0x80808080u;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                sg[q] = fmaf(xf, (float)sext8(c.v[u].x, q), sg[q]);
-                sg[q + 4] = fmaf(xf, (float)sext8(c.v[u].y, q), sg[q + 4]);
-                su[q] = fmaf(xf, (float)sext8(c.v[u].z, q), su[q]);
-                su[q + 4] = fmaf(xf, (float)sext8(c.v[u].w, q), su[q + 4]);
+                sg[q] = fmaf(xf, ubyte_f(gx, q), sg[q]);
+                sg[q + 4] = fmaf(xf, ubyte_f(gy, q), sg[q + 4]);
+                su[q] = fmaf(xf, ubyte_f(ux, q), su[q]);
+                su[q + 4] = fmaf(xf, ubyte_f(uy, q), su[q + 4]);
             }
         }
+        const float corr = 128.f * sx;
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            ag[q] += (double)sg[q];
-            au[q] += (double)su[q];
+            ag[q] += (double)(sg[q] - corr);
+            au[q] += (double)(su[q] - corr);
         }
     } else {
 #pragma unroll
@@ -730,7 +763,8 @@ template <int PK, int R, int G>
 __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     constexpr int NT = kS2Threads;
     constexpr int NW = NT / kWave;
-    extern __shared__ uint32_t dyn2[];
+    extern __shared__ uint4 dyn2v[];                     // 16-byte aligned
+    uint32_t* dyn2 = reinterpret_cast<uint32_t*>(dyn2v);
     __shared__ uint32_t hist[2048 + 64];
     __shared__ int sc[24];
     __shared__ int wc[4][NW];
@@ -851,11 +885,20 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         if (ncand <= kSmallCand) {
             bool kept = false;
             if (t < ncand) {
+                // rank = candidates before this one in (key descending, index
+                // ascending); 8 per step with two 16-byte reads (cand has 64
+                // spare words past F, and entries past ncand are masked)
                 const uint32_t v = cand[t];
                 int rank = 0;
-                for (int i = 0; i < ncand; ++i) {
-                    const uint32_t u = cand[i];
-                    rank += (u > v || (u == v && i < t)) ? 1 : 0;
+                for (int i = 0; i < ncand; i += 8) {
+                    const uint4 a4 = *reinterpret_cast<const uint4*>(cand + i);
+                    const uint4 b4 = *reinterpret_cast<const uint4*>(cand + i + 4);
+                    const uint32_t u[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int ii = i + k;
+                        rank += (ii < ncand && (u[k] > v || (u[k] == v && ii < t))) ? 1 : 0;
+                    }
                 }
                 kept = rank < need;
             }
