@@ -758,6 +758,7 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
 // while the previous group is reduced and accumulated.
 // ---------------------------------------------------------------------------
 constexpr int kSmallCand = 128;   // candidates ranked by direct comparison up to this many
+constexpr int kCandCap = 1024;    // candidates listed in LDS (more: the slow path)
 
 template <int PK, int R, int G>
 __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
@@ -774,8 +775,11 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int F = a.F, k = a.k, W2 = a.W2;
     const int r0 = (int)((long long)w * F / W2), r1 = (int)((long long)(w + 1) * F / W2);
     const int L = r1 - r0;                                 // channels of this block's range
-    uint32_t* cand = dyn2;                                 // [F + 64] candidate keys, index order
-    uint16_t* chan = reinterpret_cast<uint16_t*>(dyn2 + F + 64);   // [cap + 64] the block's list
+    uint32_t* keys = dyn2;                                 // [F + 64, to 16 B] every key, index order
+    uint32_t* cval = keys + ((F + 64 + 3) & ~3);           // [kCandCap + 64] candidate keys, index order
+    uint16_t* cidx = reinterpret_cast<uint16_t*>(cval + kCandCap + 64);   // [kCandCap + 64] their channels
+    uint16_t* kr = cidx + kCandCap + 64;                   // [kCandCap] rank among the kept candidates
+    uint16_t* chan = kr + kCandCap;                        // [cap + 64] the block's list
     const float* keyb = a.key + (size_t)b * a.f_pad;
 
     const uint32_t row_bytes = (uint32_t)a.d * 2u;
@@ -804,8 +808,14 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 #pragma unroll
         for (int q = 0; q < PK; ++q) kb[q] = valid[q] ? kb[q] : 0x80000000u;
     }
+    // every key in LDS too (index order), for the candidates' values
+    if (t * PK < F) {
+#pragma unroll
+        for (int q = 0; q < PK; q += 4)
+            if (t * PK + q < F) *reinterpret_cast<uint4*>(keys + t * PK + q) = make_uint4(kb[q], kb[q + 1], kb[q + 2], kb[q + 3]);
+    }
     // the first NT channels of the range, one per thread
-    uint32_t own0 = t < L ? __float_as_uint(keyb[r0 + t]) : 0u;
+    const uint32_t own0 = t < L ? __float_as_uint(keyb[r0 + t]) : 0u;
     if (t == 0) chan[0] = 0;                               // row 0 stands in for an empty list
 
     // ---- threshold bin
@@ -827,49 +837,52 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     auto is_cert = [&](uint32_t v) { return ((int)v >> shift) > cert_gt; };
     auto is_cand = [&](uint32_t v) { return ((int)v >> shift) == cand_eq; };
 
-    // ---- block-wide counts: certain keys (high half), candidates (low half);
-    // the exclusive scan gives each thread the index-order rank of its first
-    // certain key and its first candidate
-    int ncert_t = 0, nd = 0;
+    // ---- this thread's certain / candidate keys as bit masks, then one
+    // block scan of the counts: index-order rank of the thread's first
+    // certain key (high half) and first candidate (low half)
+    uint64_t cem = 0, cdm = 0;
 #pragma unroll
     for (int q = 0; q < PK; ++q) {
-        ncert_t += is_cert(kb[q]) ? 1 : 0;
-        nd += is_cand(kb[q]) ? 1 : 0;
+        cem |= is_cert(kb[q]) ? (1ull << q) : 0ull;
+        cdm |= is_cand(kb[q]) ? (1ull << q) : 0ull;
     }
+    const int ncert_t = __popcll(cem), nd = __popcll(cdm);
     int tot;
     const uint32_t pre = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)ncert_t << 16) | (uint32_t)nd), sc, tot);
     const int ncand = (int)((uint32_t)tot & 0xffffu);
     const int C = (int)((uint32_t)tot >> 16);            // certain keys in all
-    const int crank0 = (int)(pre >> 16);
+    const int crank0 = (int)(pre >> 16), cp0 = (int)(pre & 0xffffu);
+    const bool listed = ncand <= kCandCap;                // candidates compacted (else the slow path)
     // this block's share of the certain keys: ranks [c0, c1)
     const int c0 = (int)((long long)w * C / W2), c1 = (int)((long long)(w + 1) * C / W2);
-    const int nc = c1 - c0;
-    {
-        // candidates to cand[] and this block's certain share to chan[];
-        // lanes with nothing to write store to a per-lane dummy word
-        const int lane = t & 63;
-        uint32_t* cdummy = cand + F + lane;
-        uint16_t* sdummy = chan + (k + W2 - 1) / W2 + 2 + lane;
-        const bool share = crank0 < c1 && crank0 + ncert_t > c0;
-        const bool owns_r0 = t == r0 / PK;
-        if (nd > 0 || share || owns_r0) {
-            int cp = (int)(pre & 0xffffu), cr = crank0, cp_r0 = 0, cr_r0 = 0;
-#pragma unroll
-            for (int q = 0; q < PK; ++q) {
-                const bool ce = is_cert(kb[q]), cd = is_cand(kb[q]);
-                const bool at_r0 = t * PK + q == r0;
-                cp_r0 = at_r0 ? cp : cp_r0;                // counts before the range
-                cr_r0 = at_r0 ? cr : cr_r0;
-                *(cd ? cand + cp : cdummy) = kb[q];
-                *(ce && cr >= c0 && cr < c1 ? chan + (cr - c0) : sdummy) = (uint16_t)(t * PK + q);
-                cp += cd ? 1 : 0;
-                cr += ce ? 1 : 0;
-            }
-            if (owns_r0) {
-                sc[16] = cp_r0;
-                sc[18] = cr_r0;
+    int nc = listed ? c1 - c0 : 0;
+    if (listed) {
+        // share: the certain keys of rank [c0, c1) into chan; candidates
+        // (index order) into cidx; each lane walks only its set bits
+        if (crank0 < c1 && crank0 + ncert_t > c0) {
+            uint64_t m = cem;
+            int cr = crank0;
+            while (m) {
+                const int q = __builtin_ctzll(m);
+                m &= m - 1;
+                if (cr >= c0 && cr < c1) chan[cr - c0] = (uint16_t)(t * PK + q);
+                ++cr;
             }
         }
+        uint64_t m = cdm;
+        int cp = cp0;
+        while (m) {
+            const int q = __builtin_ctzll(m);
+            m &= m - 1;
+            cidx[cp] = (uint16_t)(t * PK + q);
+            cval[cp++] = keys[t * PK + q];                 // written by this thread above
+        }
+    }
+    if (t == r0 / PK) {                                    // counts before the range
+        const int below = r0 - t * PK;                     // keys of this thread before r0
+        const uint64_t lo = below >= 64 ? ~0ull : ((1ull << below) - 1);
+        sc[16] = cp0 + __popcll(cdm & lo);
+        sc[18] = crank0 + __popcll(cem & lo);
     }
     lds_barrier();
     const int cs = sc[16];                                 // candidates before the range
@@ -878,91 +891,118 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     RowGroup<R, G> cur, nxt;
     load_group<R, G>(rs, chan, 0, E, row_bytes, mat_bytes, voff, cur);
 
-    // ---- resolve the candidates while those loads are in flight: cand[i]
-    // gets bit 31 when kept
-    if (ncand > 0) {
-        const int need = st.krem;                         // candidates to keep
-        if (ncand <= kSmallCand) {
-            bool kept = false;
-            if (t < ncand) {
-                // rank = candidates before this one in (key descending, index
-                // ascending); 8 per step with two 16-byte reads (cand has 64
-                // spare words past F, and entries past ncand are masked)
-                const uint32_t v = cand[t];
-                int rank = 0;
-                for (int i = 0; i < ncand; i += 8) {
-                    const uint4 a4 = *reinterpret_cast<const uint4*>(cand + i);
-                    const uint4 b4 = *reinterpret_cast<const uint4*>(cand + i + 4);
-                    const uint32_t u[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+    int nks = 0, kc_before = 0;
+    if (listed) {
+        // ---- resolve the candidates while those loads are in flight:
+        // cidx[i] gets bit 15 when kept
+        if (ncand > 0) {
+            const int need = st.krem;                     // candidates to keep
+            if (ncand <= kSmallCand) {
+                bool kept = false;
+                if (t < ncand) {
+                    // rank = candidates before this one in (key descending,
+                    // index ascending), 8 per step (cidx has 64 spare entries;
+                    // entries past ncand are masked)
+                    const uint32_t v = cval[t];
+                    int rank = 0;
+                    for (int i = 0; i < ncand; i += 8) {
+                        const uint4 a4 = *reinterpret_cast<const uint4*>(cval + i);
+                        const uint4 b4 = *reinterpret_cast<const uint4*>(cval + i + 4);
+                        const uint32_t u[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const int ii = i + k;
-                        rank += (ii < ncand && (u[k] > v || (u[k] == v && ii < t))) ? 1 : 0;
+                        for (int kk = 0; kk < 8; ++kk) {
+                            const int ii = i + kk;
+                            rank += (ii < ncand && (u[kk] > v || (u[kk] == v && ii < t))) ? 1 : 0;
+                        }
                     }
+                    kept = rank < need;
                 }
-                kept = rank < need;
+                lds_barrier();
+                if (kept) cidx[t] |= 0x8000u;
+            } else {
+                // many candidates: remaining bits by histogram over the keys
+                // of the threshold bin, then ties in index order
+                SelectState s2 = st;
+                s2.ncand = F;
+                uint32_t T;
+                int cgt;
+                block_select_refine<NT>(s2, keys, T, cgt, hist, sc);
+                const int eq_need = k - cgt;
+                int eq_run = 0;
+                for (int i0 = 0; i0 < ncand; i0 += NT) {
+                    const int i = i0 + t;
+                    const uint32_t v = i < ncand ? cval[i] : 0u;
+                    bool p[1] = {i < ncand && v == T};
+                    int pos[1], tt[1];
+                    block_ballot_pos<kS2Threads, 1>(p, wc, pos, tt);
+                    if (i < ncand && (v > T || (p[0] && eq_run + pos[0] < eq_need))) cidx[i] |= 0x8000u;
+                    eq_run += tt[0];
+                }
             }
             lds_barrier();
-            if (kept) cand[t] |= 0x80000000u;
-        } else {
-            SelectState s2 = st;
-            s2.ncand = ncand;
-            uint32_t T;
-            int cgt;
-            block_select_refine<NT>(s2, cand, T, cgt, hist, sc);
-            // kept: above T, or equal to T and among the first k - cgt equal ones
-            const int eq_need = k - cgt;
-            int eq_run = 0;
-            for (int i0 = 0; i0 < ncand; i0 += NT) {
-                const int i = i0 + t;
-                const uint32_t v = i < ncand ? cand[i] : 0u;
-                bool p[1] = {i < ncand && v == T};
-                int pos[1], tt[1];
-                block_ballot_pos<kS2Threads, 1>(p, wc, pos, tt);
-                if (i < ncand && (v > T || (p[0] && eq_run + pos[0] < eq_need))) cand[i] = v | 0x80000000u;
-                eq_run += tt[0];
-            }
         }
-        lds_barrier();
-    }
-    // ---- kept candidates: this block's share (ranks [s0, s1) among them, in
-    // index order) goes after its certain entries; count those before the range
-    int nks = 0, kc_before = 0;
-    {
+        // ---- kept candidates: this block's share (ranks [s0, s1) among them,
+        // in index order) goes after its certain entries; count those before
+        // the range.  Ranks are found first, the writes follow (the shares of
+        // later chunks need the totals of earlier ones only).
         int run = 0;
         for (int i0 = 0; i0 < ncand; i0 += NT) {
             const int i = i0 + t;
-            const bool kept = i < ncand && (cand[i] >> 31) != 0;
+            const bool kept = i < ncand && (cidx[i] & 0x8000u) != 0;
             bool p[2] = {kept, kept && i < cs};
             int pos[2], tt[2];
             block_ballot_pos<kS2Threads, 2>(p, wc, pos, tt);
-            pos[0] += run;
+            if (i < ncand) kr[i] = (uint16_t)(run + pos[0]);   // rank among the kept
             run += tt[0];
             kc_before += tt[1];
-            if (kept) cand[i] = 0x80000000u | (uint32_t)pos[0];   // the flag, and the rank
         }
-        if (ncand > 0) lds_barrier();
         const int KC = run;
         const int s0 = (int)((long long)w * KC / W2), s1 = (int)((long long)(w + 1) * KC / W2);
         nks = s1 - s0;
-        // the owners of the candidates place this block's share
-        if (nd > 0 && s1 > s0) {
-            uint16_t* sdummy = chan + (k + W2 - 1) / W2 + 2 + (t & 63);
-            int cp = (int)(pre & 0xffffu);
-#pragma unroll
-            for (int q = 0; q < PK; ++q) {
-                const bool cd = is_cand(kb[q]);
-                const uint32_t v = cand[cp];                // cp <= ncand: in bounds
-                const int r = (int)(v & 0x7fffffffu);
-                *(cd && (v >> 31) && r >= s0 && r < s1 ? chan + (nc + r - s0) : sdummy) = (uint16_t)(t * PK + q);
-                cp += cd ? 1 : 0;
-            }
+        for (int i = t; i < ncand; i += NT) {
+            const int r = kr[i];
+            if ((cidx[i] & 0x8000u) && r >= s0 && r < s1) chan[nc + r - s0] = cidx[i] & 0x7fffu;
         }
+    } else {
+        // ---- slow path (more candidates than the list holds): the exact
+        // threshold over all keys, then every kept key's rank by one packed
+        // scan; this block streams kept ranks [w*k/W2, (w+1)*k/W2)
+        SelectState s2 = st;
+        s2.ncand = F;
+        uint32_t T;
+        int cgt;
+        block_select_refine<NT>(s2, keys, T, cgt, hist, sc);
+        const int need = k - cgt;
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int q = 0; q < PK; ++q) {
+            gt += (int)kb[q] >= 0 && kb[q] > T ? 1 : 0;
+            eq += kb[q] == T ? 1 : 0;
+        }
+        int tk;
+        const uint32_t pk = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)gt << 16) | (uint32_t)eq), sc, tk);
+        int eb = (int)(pk & 0xffffu);
+        int pos = (int)(pk >> 16) + min(eb, need);
+        const int k0 = (int)((long long)w * k / W2), k1 = (int)((long long)(w + 1) * k / W2);
+#pragma unroll
+        for (int q = 0; q < PK; ++q) {
+            const bool e = kb[q] == T;
+            const bool on = ((int)kb[q] >= 0 && kb[q] > T) || (e && eb < need);
+            if (on && pos >= k0 && pos < k1) chan[pos - k0] = (uint16_t)(t * PK + q);
+            const int j = t * PK + q;
+            if (j >= r0 && j < r1) {
+                if (on && a.idx) a.idx[(size_t)b * k + pos] = j;
+                if (a.mask) a.mask[(size_t)b * F + j] = on ? 1 : 0;
+            }
+            eb += e ? 1 : 0;
+            pos += on ? 1 : 0;
+        }
+        nc = k1 - k0;
     }
     const int kept_before = cert_before + kc_before;
 
     // ---- the range: kept flags, idx and mask
-    if (a.idx || a.mask) {
+    if (listed && (a.idx || a.mask)) {
         int nk = 0, nd_run = 0;
         for (int c0r = 0; c0r < L; c0r += NT) {
             const int j = r0 + c0r + t;
@@ -971,7 +1011,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             bool p1[1] = {in && is_cand(v)};
             int pos1[1], t1[1];
             block_ballot_pos<kS2Threads, 1>(p1, wc, pos1, t1);
-            const bool kc = p1[0] && (cand[cs + nd_run + pos1[0]] >> 31) != 0;
+            const bool kc = p1[0] && (cidx[cs + nd_run + pos1[0]] & 0x8000u) != 0;
             bool p2[1] = {in && (is_cert(v) || kc)};
             int pos2[1], t2[1];
             block_ballot_pos<kS2Threads, 1>(p2, wc, pos2, t2);
@@ -981,8 +1021,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             nk += t2[0];
         }
     }
-    const int nkc = nks;
-    const int n = nc + nkc;
+    const int n = nc + nks;
     lds_barrier();
 
     // ---- sparse SwiGLU: group 0 = entries [0, E), then [E, n) G at a time.
@@ -1019,7 +1058,8 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 template <int PK, int R, int G>
 static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     const int cap = (a.k + a.W2 - 1) / a.W2 + 2;          // list length bound: ceil(C/W2) + ceil(KC/W2)
-    const size_t dyn = ((size_t)a.F + 64) * 4 + ((size_t)cap + 64) * 2;
+    const size_t dyn = ((size_t)(a.F + 64 + 3) & ~(size_t)3) * 4 + ((size_t)kCandCap + 64) * 4 +
+                       ((size_t)kCandCap * 2 + 64 + cap + 64) * 2;
     auto fn = k_stage2<PK, R, G>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);

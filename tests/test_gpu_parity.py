@@ -134,3 +134,42 @@ def test_stale_workspace_still_exact():
         again = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 700, workspace=ws)
         for u, v in zip(again, ref):
             assert torch.equal(u, v), fill
+
+
+def _pattern_case(d, F, n_patterns, seed, kind="int8"):
+    # Channels copy one of a few weight rows, so their ranking keys coincide in
+    # large groups: the threshold bin then holds hundreds or thousands of
+    # exactly equal keys, and the lower index must win among them.
+    from _gpu_common import Case
+    from prox_workloads import bf16_round
+    r = np.random.default_rng([seed, 4242, d, F])
+    pats = {n: r.standard_normal((n_patterns, d), dtype=np.float32) * np.float32(0.05)
+            for n in ("wg_t", "wu_t")}
+    pick = r.integers(0, n_patterns, F)
+    wg = bf16_round(pats["wg_t"][pick])
+    wu = bf16_round(pats["wu_t"][pick])
+    wd = bf16_round(r.standard_normal((F, d), dtype=np.float32) * np.float32(0.02))
+    x = bf16_round(r.laplace(0.0, 1.0, size=(2, d)).astype(np.float32))
+    return Case(x, wg, wu, wd, kind)
+
+
+@pytest.mark.parametrize("F,n_patterns", [(2048, 3), (4096, 3), (8192, 3)])
+def test_many_equal_keys(F, n_patterns):
+    # F=2048: ~680 equal keys per value (ranked by histogram + index order);
+    # F=4096, 8192: ~1365 / ~2730 per value, more than the candidate list
+    # holds (the path that ranks every key with one block scan)
+    import free_ffn_activation_prox_amd as P
+    from oracle import prox_oracle as O
+    d = 256
+    c = _pattern_case(d, F, n_patterns, seed=F)
+    for sp in (50, 70, 90):
+        k_in, k_ff = pct_count(d, 60), pct_count(F, 100 - sp)
+        st = c.check(k_in, k_ff, label=f"patterns F={F} sp={sp}")
+        _report(f"patterns F={F} sp={sp}", st)
+        assert st["key_bits_differ"] == 0
+        # equal keys: the selection must match the oracle's exactly
+        _, mask, _ = P.ffn_forward(c.dx, c.weights, c.proxy, k_in, k_ff)
+        pg, pu = c.oracle_proxies()
+        for b in range(c.B):
+            omask = O.stage1_token(c.x[b], pg, pu, k_in, k_ff)[5]
+            assert np.array_equal(np.flatnonzero(mask[b].cpu().numpy()), np.asarray(omask)), (F, sp, b)
