@@ -189,17 +189,43 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
 
     hipError_t e = mark(0);
     if (e != hipSuccess) return hip_fail(e, "event record");
+    unsigned long long* tcnt = reinterpret_cast<unsigned long long*>(ws + L.tcnt);
+    const uint16_t* wg = static_cast<const uint16_t*>(w->w_gate_t);
+    const uint16_t* wu = static_cast<const uint16_t*>(w->w_up_t);
+    const uint16_t* wd = static_cast<const uint16_t*>(w->w_down);
+
+    if (batch >= kBatchMin) {
+        // matrix-core path: input selection and proxy GEMM over the batch,
+        // per-token channel selection, gate/up and down over the tokens' masks
+        uint16_t* xm = reinterpret_cast<uint16_t*>(ws + L.xm);
+        uint8_t* bmask = mask ? mask : ws + L.bmask;
+        uint16_t* hb = reinterpret_cast<uint16_t*>(ws + L.hb);
+        e = launch_xsel(xb, batch, d, k_in, xm, taps ? taps->in_idx : nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "input selection");
+        e = launch_proxy_batch(xm, batch, d, pv, reinterpret_cast<float*>(ws + L.bpart), tcnt, next_call_tag(),
+                               key, gh, taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "proxy GEMM");
+        if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
+        e = launch_select(key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, bmask, s);
+        if (e != hipSuccess) return hip_fail(e, "channel selection");
+        int ks = 0;
+        e = launch_stage2_batch(xb, wg, wu, wd, bmask, hb, batch, d, F, g.f_pad, ypart, &ks, s);
+        if (e != hipSuccess) return hip_fail(e, "stage 2 (batch)");
+        if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
+        e = launch_reduce_y(ypart, batch, d, ks, y, gh, s);
+        if (e != hipSuccess) return hip_fail(e, "reduce y");
+        if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
+        return PROX_OK;
+    }
+
     const S1Geom g1 = s1_geom(k_in, F, p->kind, batch, n_cu);
     double* part = reinterpret_cast<double*>(ws + L.part);
-    unsigned long long* tcnt = reinterpret_cast<unsigned long long*>(ws + L.tcnt);
     e = launch_stage1(xb, batch, d, k_in, pv, key, gh, part, tcnt, next_call_tag(), g1,
                       taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr,
                       taps ? taps->in_idx : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "stage 1");
     if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
-    e = launch_stage2(xb, static_cast<const uint16_t*>(w->w_gate_t),
-                      static_cast<const uint16_t*>(w->w_up_t), static_cast<const uint16_t*>(w->w_down),
-                      key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart, s);
+    e = launch_stage2(xb, wg, wu, wd, key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart, s);
     if (e != hipSuccess) return hip_fail(e, "stage 2");
     if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_reduce_y(ypart, batch, d, W2, y, gh, s);

@@ -1,0 +1,761 @@
+// Prox sparse SwiGLU FFN for batches of 8 or more tokens (gfx950 matrix cores).
+//
+// Each token keeps its own input set and its own channel mask (Prox, Abstract:
+// Stage 1 ranks channels per token, one mask shared by the three projections;
+// tokens are independent problems).  At 8+ tokens nearly every input row and
+// every channel is kept by some token, so both stages become contractions over
+// the union, run on bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
+//
+//   input select  x~_b = x_b on its k_in largest |x| (lower index wins ties),
+//                 0 elsewhere
+//   proxy GEMM    g~ = X~ W~_gate, u~ = X~ W~_up over the quantized proxy.
+//                 Codes are small integers and x is bf16, so every product is
+//                 exact in fp32; the unit accumulates 32 of them, and those
+//                 sums are added in fp64 (int4: times the group scale first).
+//                 key = fp32(|silu(g~) u~|) with h~ formed in fp64.
+//   selection     the per-token top-k_ff over the keys (the same kernel as the
+//                 single-token path, selection only)
+//   gate/up       G = X W_gate, U = X W_up over the channels some token keeps
+//                 (PrunePath, §2.1, Eq. (1)); h = silu(g) u where the token
+//                 keeps the channel, 0 elsewhere, stored as bf16 hi + lo
+//   down          y = H W_down (COUNTDOWN, Abstract: y combines W_down rows
+//                 weighted by h), hi and lo halves as two products, partial
+//                 sums per channel slice, then the fixed-order reduction
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, r = l % 16, q = l / 16):
+//   A[r][8q .. 8q + 7], B[8q .. 8q + 7][r], C[4q + i][r] for i < 4.
+// The proxy codes and W_down are stored with the reduced dimension slowest,
+// so their tiles are transposed through LDS on the way in.
+#include "prox_device.hpp"
+#include "prox_internal.hpp"
+
+namespace prox {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// Keeps a value in registers at this point of the program (no code emitted):
+// stops the compiler from sinking the accumulation below the next loads.
+template <int N>
+__device__ __forceinline__ void settle_acc(f32x4_t (&v)[N]) {
+#pragma unroll
+    for (int g = 0; g < N; ++g) asm volatile("" : "+v"(v[g]) : : "memory");
+}
+
+// Round to nearest even, finite inputs.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two rows' small integers -> one dword of two bf16 (row a low, row b high).
+// The integers are exact in fp32 and in bf16, so the high half is the value.
+__device__ __forceinline__ uint32_t pair_bf16(int qa, int qb) {
+    return __builtin_amdgcn_perm(__float_as_uint((float)qb), __float_as_uint((float)qa), 0x07060302u);
+}
+
+// ===========================================================================
+// Input selection: one block per token.  Thread t holds x[16t .. 16t + 15].
+// Keys are |x| as bf16 bits (sign cleared), so the order of keys is the order
+// of magnitudes; T = the k-th largest key, all keys above T are kept and the
+// keys equal to T are kept in index order until k are kept.
+// ===========================================================================
+constexpr int kXselThreads = 1024;
+constexpr int kXselPer = 16;   // d <= 16384
+
+__global__ void __launch_bounds__(kXselThreads) k_xsel(const uint16_t* __restrict__ x, int d, int k,
+                                                      uint16_t* __restrict__ xm, int32_t* __restrict__ in_idx) {
+    __shared__ uint32_t hist[2049];
+    __shared__ int sc[32];
+    const int b = blockIdx.x, t = threadIdx.x;
+    uint32_t v[kXselPer], key[kXselPer];
+    bool valid[kXselPer];
+    load_u16_contig<kXselPer>(x + (size_t)b * d, d, d, v, valid);
+#pragma unroll
+    for (int q = 0; q < kXselPer; ++q) key[q] = valid[q] ? (v[q] & 0x7fffu) : 0u;
+
+    const bool all = k >= d, none = k <= 0;   // uniform over the block
+    uint32_t T = 0;
+    int cgt = 0;
+    if (!all && !none) {
+        SelectState st = block_coarse_bin<kXselPer, kXselThreads>(key, valid, k, 15, hist, sc);
+        if (st.shift > 0) {
+            const int nb = 1 << st.shift;
+            for (int i = t; i < nb; i += kXselThreads) hist[i] = 0u;
+            lds_barrier();
+#pragma unroll
+            for (int q = 0; q < kXselPer; ++q)
+                if (valid[q] && (key[q] >> st.shift) == st.prefix) atomicAdd(&hist[key[q] & (nb - 1)], 1u);
+            lds_barrier();
+            uint32_t digit;
+            int ab;
+            find_bin<kXselThreads>(hist, nb, st.krem, sc, digit, ab);
+            T = (st.prefix << st.shift) | digit;
+            cgt = st.above + ab;
+        } else {
+            T = st.prefix;
+            cgt = st.above;
+        }
+    }
+    const int need = k - cgt;   // keys equal to T that are kept, lowest indices first
+    int neq = 0;
+#pragma unroll
+    for (int q = 0; q < kXselPer; ++q) neq += (valid[q] && key[q] == T) ? 1 : 0;
+    int tot;
+    int eq_before = block_excl_scan<kXselThreads>(neq, sc, tot);
+    bool keep[kXselPer];
+    int nk = 0;
+#pragma unroll
+    for (int q = 0; q < kXselPer; ++q) {
+        const bool eq = valid[q] && key[q] == T;
+        keep[q] = valid[q] && (all || (!none && (key[q] > T || (eq && eq_before < need))));
+        eq_before += eq ? 1 : 0;
+        nk += keep[q] ? 1 : 0;
+    }
+    int pos = block_excl_scan<kXselThreads>(nk, sc, tot);
+    const int base = t * kXselPer;
+#pragma unroll
+    for (int q = 0; q < kXselPer; q += 8) {
+        if (base + q < d) {
+            uint32_t wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wv[e] = (keep[q + 2 * e] ? v[q + 2 * e] : 0u) | ((keep[q + 2 * e + 1] ? v[q + 2 * e + 1] : 0u) << 16);
+            *reinterpret_cast<uint4*>(xm + (size_t)b * d + base + q) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+    }
+    if (in_idx) {
+#pragma unroll
+        for (int q = 0; q < kXselPer; ++q)
+            if (keep[q]) in_idx[(size_t)b * k + pos++] = base + q;
+    }
+}
+
+hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,
+                       hipStream_t s) {
+    hipLaunchKernelGGL(k_xsel, dim3(B), dim3(kXselThreads), 0, s, x, d, k_in, xm, in_idx);
+    return hipGetLastError();
+}
+
+// ===========================================================================
+// Proxy GEMM.  Block (tile, split): the tile's TC channels (64 int8 / 128
+// int4) over rows [r0, r1) of the split, every token.  Rows go 64 at a time
+// ("stages"): each thread loads two rows of one 16-byte column block of the
+// tile, turns its codes into bf16 and writes them to LDS transposed,
+// [mat][channel][row]; the MFMA A operand (16 channels x 8 rows per lane) is
+// then one 16-byte LDS read.  B is x~ (token-major, rows contiguous), read
+// from global memory.  Wave w owns M-tiles (16 channels) w*MT/4 .. of both
+// matrices, so each lane ends with gate and up of the same channels.
+//
+// LDS rows are 72 bf16 (64 + 8 padding) and the 16-byte chunks of a channel
+// row are permuted by (chunk ^ column block), which spreads both the
+// transposing writes and the operand reads over the banks.
+// ===========================================================================
+struct PbArgs {
+    const uint16_t* xm;       // [B][d] x~
+    const uint8_t* codes;     // [tiles][d][128 B]
+    const float* scales;      // gate [groups][f_pad], up [groups][f_pad]
+    int B, d, F, f_pad, groups, tiles, ks1, rps;
+    float* part;              // [ks1][2][B][f_pad] split partial sums (ks1 > 1)
+    unsigned long long* tcnt; // [tiles] arrival counters
+    uint32_t gen;
+    float* key;               // [B][f_pad]
+    uint32_t* gh;             // [B][kGhBins]
+    double* h_tap;            // [B][F] or null
+    float* key_tap;           // [B][F] or null
+};
+
+constexpr int kPbRS = 72;     // LDS row stride of the transposed tiles, in bf16
+constexpr int kPbDepth = 4;   // stages in flight per thread
+
+template <int NG>
+struct PbStage {
+    uint4 c[2];         // rows 2p, 2p + 1 of this thread's column block
+    uint4 x[2][NG];     // B operands of the stage's two K-steps
+};
+
+__device__ __forceinline__ void pb_score(const PbArgs& a, int b, int j, double g, double u) {
+    const double h = g / (1.0 + exp(-g)) * u;
+    const float kf = (float)fabs(h);
+    a.key[(size_t)b * a.f_pad + j] = kf;
+    __hip_atomic_fetch_add(a.gh + (size_t)b * kGhBins + (__float_as_uint(kf) >> kGhShift), 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.h_tap) a.h_tap[(size_t)b * a.F + j] = h;
+    if (a.key_tap) a.key_tap[(size_t)b * a.F + j] = kf;
+}
+
+template <int KIND, int NG>
+__global__ void __launch_bounds__(256) k_proxy_batch(PbArgs a) {
+    constexpr int TC = KIND == 1 ? 64 : 128;   // channels of a tile
+    constexpr int CPB = TC / 8;                // channels per 16-byte column block (per matrix)
+    constexpr int MT = TC / 16;                // M-tiles per matrix
+    constexpr int MW = MT / 4;                 // M-tiles per wave
+    constexpr int TILE = 2 * TC * kPbRS;       // bf16 per LDS buffer
+    __shared__ uint4 lds_raw[2 * TILE / 8];
+    __shared__ int flag;
+    uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int r = l & 15, q4 = l >> 4;
+    const int tile = blockIdx.x / a.ks1, split = blockIdx.x % a.ks1;
+    const int d = a.d;
+    const int r0 = split * a.rps, r1 = min(d, r0 + a.rps);
+
+    // loads: thread t -> column block cb, rows 2p, 2p + 1 of each stage
+    const int cb = t & 7, p = t >> 3;
+    const uint32_t codes_bytes = (uint32_t)a.tiles * (uint32_t)d * kTileRowBytes;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, codes_bytes);
+    const uint32_t tile_off = (uint32_t)tile * (uint32_t)d * kTileRowBytes;
+    const uint32_t x_bytes = (uint32_t)a.B * (uint32_t)d * 2u;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xm, x_bytes);
+    uint32_t xrow[NG];   // byte offset of this lane's B-operand token row, or past the end
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int n = 16 * g + r;
+        xrow[g] = n < a.B ? (uint32_t)n * (uint32_t)d * 2u : x_bytes;
+    }
+
+    auto load_stage = [&](int s, PbStage<NG>& st) {
+        const int ra = r0 + 64 * s + 2 * p;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = ra + h;
+            st.c[h] = buf_load16(rc, row < r1 ? (uint32_t)row * kTileRowBytes + cb * 16u : codes_bytes, tile_off);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int row = r0 + 64 * s + 32 * ks + 8 * q4;
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                st.x[ks][g] = buf_load16(rx, (row < r1 && xrow[g] < x_bytes) ? xrow[g] + (uint32_t)row * 2u : x_bytes, 0);
+        }
+    };
+
+    // codes of rows 2p, 2p + 1 -> bf16 pairs at [mat][channel][rows 2p, 2p + 1]
+    auto store_stage = [&](const PbStage<NG>& st, uint16_t* buf) {
+        const uint32_t ca[4] = {st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w};
+        const uint32_t cbv[4] = {st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w};
+        const int chunk = (p >> 2) ^ cb, sub = 2 * (p & 3);
+#pragma unroll
+        for (int mat = 0; mat < 2; ++mat) {
+#pragma unroll
+            for (int e = 0; e < CPB; ++e) {
+                int qa, qb;
+                if (KIND == 1) {
+                    qa = __builtin_amdgcn_sbfe((int)ca[2 * mat + e / 4], 8 * (e % 4), 8);
+                    qb = __builtin_amdgcn_sbfe((int)cbv[2 * mat + e / 4], 8 * (e % 4), 8);
+                } else {
+                    qa = __builtin_amdgcn_sbfe((int)ca[2 * mat + e / 8], 4 * (e % 8), 4);
+                    qb = __builtin_amdgcn_sbfe((int)cbv[2 * mat + e / 8], 4 * (e % 8), 4);
+                }
+                const int ch = CPB * cb + e;
+                *reinterpret_cast<uint32_t*>(buf + (mat * TC + ch) * kPbRS + 8 * chunk + sub) = pair_bf16(qa, qb);
+            }
+        }
+    };
+
+    f32x4_t acc[2 * MW][NG];   // [mat * MW + tile of the wave][token group]
+    double dacc[2 * MW][NG][4];
+#pragma unroll
+    for (int c = 0; c < 2 * MW; ++c)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            acc[c][g] = zero4();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dacc[c][g][i] = 0.0;
+        }
+
+    auto mma_stage = [&](const PbStage<NG>& st, const uint16_t* buf) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int c = 0; c < 2 * MW; ++c) {
+                const int mat = c / MW, mt = w * MW + c % MW;
+                const int ch = 16 * mt + r;
+                const int chunk = (4 * ks + q4) ^ ((ch / CPB) & 7);
+                const uint4 av = *reinterpret_cast<const uint4*>(buf + (mat * TC + ch) * kPbRS + 8 * chunk);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) acc[c][g] = mfma16(av, st.x[ks][g], acc[c][g]);
+            }
+        }
+    };
+
+    // every 128 rows: fp32 sums -> fp64 (int4: times the group's scales)
+    auto flush = [&](int grp) {
+#pragma unroll
+        for (int c = 0; c < 2 * MW; ++c) {
+            const int mat = c / MW, mt = w * MW + c % MW;
+            float4 sv = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (KIND == 2) {
+                const int gi = min(grp, a.groups - 1);
+                sv = *reinterpret_cast<const float4*>(a.scales + ((size_t)mat * a.groups + gi) * a.f_pad +
+                                                     tile * TC + 16 * mt + 4 * q4);
+            }
+            const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dacc[c][g][i] += KIND == 2 ? (double)acc[c][g][i] * (double)s4[i] : (double)acc[c][g][i];
+                acc[c][g] = zero4();
+            }
+        }
+    };
+
+    const int nst = (r1 - r0 + 63) / 64;
+    PbStage<NG> ring[kPbDepth];
+#pragma unroll
+    for (int i = 0; i < kPbDepth; ++i) load_stage(i, ring[i]);
+    // stages past nst read zeros (past r1), so the loop runs whole rounds of
+    // kPbDepth stages with unconditional loads
+    for (int s0 = 0; s0 < nst; s0 += kPbDepth) {
+#pragma unroll
+        for (int i = 0; i < kPbDepth; ++i) {
+            uint16_t* buf = lds + (i & 1) * TILE;
+            store_stage(ring[i], buf);
+            lds_barrier();
+            mma_stage(ring[i], buf);
+            load_stage(s0 + i + kPbDepth, ring[i]);
+            if (i & 1) flush((r0 + 64 * (s0 + i)) / 128);
+        }
+    }
+
+    // this lane: gate / up of channels 16 mt + 4 q4 + i, tokens 16 g + r
+    if (a.ks1 > 1) {
+        // publish this split's sums; the block that completes the tile adds the
+        // splits in order (device-scope stores and loads, coherent across the
+        // chip's L2 caches; the stores complete before the arrival is counted)
+#pragma unroll
+        for (int c = 0; c < 2 * MW; ++c) {
+            const int mat = c / MW, mt = w * MW + c % MW;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int n = 16 * g + r;
+                if (n < a.B) {
+                    float* dst = a.part + (((size_t)split * 2 + mat) * a.B + n) * a.f_pad + tile * TC + 16 * mt + 4 * q4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        __hip_atomic_store(dst + i, (float)dacc[c][g][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
+        __syncthreads();
+        if (t == 0) {
+            unsigned long long* cnt = a.tcnt + tile;
+            unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (;;) {
+                const unsigned long long nxt =
+                    (cur >> 32) == a.gen ? cur + 1 : (((unsigned long long)a.gen << 32) | 1ull);
+                if (__hip_atomic_compare_exchange_strong(cnt, &cur, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT)) {
+                    flag = (int)(nxt & 0xffffffffull) == a.ks1 ? 1 : 0;
+                    break;
+                }
+            }
+        }
+        lds_barrier();
+        if (!flag) return;
+#pragma unroll
+        for (int c = 0; c < 2 * MW; ++c) {
+            const int mat = c / MW, mt = w * MW + c % MW;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int n = 16 * g + r;
+                if (n < a.B) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        double sum = 0.0;
+                        for (int sp = 0; sp < a.ks1; ++sp)
+                            sum += (double)__hip_atomic_load(
+                                a.part + (((size_t)sp * 2 + mat) * a.B + n) * a.f_pad + tile * TC + 16 * mt + 4 * q4 + i,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        dacc[c][g][i] = sum;
+                    }
+                }
+            }
+        }
+    }
+    // scores: c < MW are gate tiles, c + MW the up tiles of the same channels
+#pragma unroll
+    for (int c = 0; c < MW; ++c) {
+        const int mt = w * MW + c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = tile * TC + 16 * mt + 4 * q4 + i;
+            if (j >= a.F) continue;
+            double sg = 1.0, su = 1.0;
+            if (KIND == 1) {
+                sg = (double)a.scales[j];
+                su = (double)a.scales[a.f_pad + j];
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int n = 16 * g + r;
+                if (n < a.B) pb_score(a, n, j, dacc[c][g][i] * sg, dacc[c + MW][g][i] * su);
+            }
+        }
+    }
+}
+
+// Row splits of the proxy GEMM: enough blocks to cover the chip about once
+// (tiles * splits >= kPbBlocks), splits of whole 128-row groups, at most
+// kPbMaxSplits.  Depends on the shape only (the workspace is sized from it).
+constexpr int kPbBlocks = 320;
+constexpr int kPbMaxSplits = 8;
+
+PbSplit proxy_batch_split(int d, int F, int kind) {
+    const int tiles = f_pad_of(F, kind) / tile_channels(kind);
+    const int groups = (d + 127) / 128;
+    int ks = (kPbBlocks + tiles - 1) / tiles;
+    if (ks > kPbMaxSplits) ks = kPbMaxSplits;
+    if (ks > groups) ks = groups;
+    if (ks < 1) ks = 1;
+    const int gps = (groups + ks - 1) / ks;   // groups per split
+    PbSplit r;
+    r.rps = gps * 128;
+    r.ks1 = (d + r.rps - 1) / r.rps;
+    return r;
+}
+
+template <int KIND, int NG>
+static hipError_t go_proxy_batch(const PbArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL((k_proxy_batch<KIND, NG>), dim3(a.tiles * a.ks1), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int KIND>
+static hipError_t proxy_batch_ng(const PbArgs& a, hipStream_t s) {
+    const int ng = (a.B + 15) / 16;
+    if (ng == 1) return go_proxy_batch<KIND, 1>(a, s);
+    if (ng == 2) return go_proxy_batch<KIND, 2>(a, s);
+    if (ng == 3) return go_proxy_batch<KIND, 3>(a, s);
+    return go_proxy_batch<KIND, 4>(a, s);
+}
+
+hipError_t launch_proxy_batch(const uint16_t* xm, int B, int d, const ProxyView& p, float* part,
+                              unsigned long long* tcnt, uint32_t gen, float* key, uint32_t* gh,
+                              double* h_tap, float* key_tap, hipStream_t s) {
+    const PbSplit sp = proxy_batch_split(d, p.F, p.kind);
+    PbArgs a{xm, p.codes, p.scales, B, d, p.F, p.f_pad, p.groups, p.f_pad / tile_channels(p.kind),
+             sp.ks1, sp.rps, part, tcnt, gen, key, gh, h_tap, key_tap};
+    return p.kind == 1 ? proxy_batch_ng<1>(a, s) : proxy_batch_ng<2>(a, s);
+}
+
+// ===========================================================================
+// Gate/up.  Block: 16 channels j0 .. j0 + 15 (the MFMA's M), every token (N,
+// 16 per group), K = d split over the 4 waves in interleaved 32-wide steps.
+// Weight rows and x are K-contiguous, so both operands are 16-byte buffer
+// loads straight into registers; channels that no token keeps, tokens past B
+// and columns past d read at an offset past the end (zeros, no traffic).
+// Four K-steps per stage, two stages in flight; the 4 waves' sums are added
+// in LDS in a fixed order.
+// ===========================================================================
+struct GuArgs {
+    const uint16_t* x;      // [B][d]
+    const uint16_t* wg_t;   // [F][d]
+    const uint16_t* wu_t;
+    const uint8_t* mask;    // [B][F]
+    uint16_t* hb;           // [2][B][f_pad] h as bf16 hi, lo
+    int B, d, F, f_pad;
+};
+
+constexpr int kGuSteps = 4;
+
+template <int NG>
+struct GuStage {
+    uint4 g[kGuSteps], u[kGuSteps], x[kGuSteps][NG];
+};
+
+template <int NG>
+__global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
+    __shared__ uint32_t used[16];
+    __shared__ float red[4][NG][2][4][64];
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int r = l & 15, q4 = l >> 4;
+    const int j0 = blockIdx.x * 16;
+    const int d = a.d;
+
+    // channels of this block that some token keeps
+    if (t < 16) used[t] = 0u;
+    __syncthreads();
+    {
+        const int jr = j0 + (t & 15);
+        uint32_t any = 0;
+        if (jr < a.F)
+            for (int n = t >> 4; n < a.B; n += 16) any |= a.mask[(size_t)n * a.F + jr];
+        if (any) used[t & 15] = 1u;
+    }
+    __syncthreads();
+
+    const uint32_t row_bytes = (uint32_t)d * 2u;
+    const uint32_t w_bytes = (uint32_t)a.F * row_bytes, x_bytes = (uint32_t)a.B * row_bytes;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.wg_t, w_bytes), ru = make_rsrc(a.wu_t, w_bytes);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, x_bytes);
+    const int j = j0 + r;
+    const uint32_t woff = (j < a.F && used[r]) ? (uint32_t)j * row_bytes : w_bytes;
+    uint32_t xoff[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int n = 16 * g + r;
+        xoff[g] = n < a.B ? (uint32_t)n * row_bytes : x_bytes;
+    }
+    const int kl = 32 * w + 8 * q4;   // this lane's first column within a 128-wide step
+
+    auto load = [&](int kb, GuStage<NG>& st) {
+#pragma unroll
+        for (int s = 0; s < kGuSteps; ++s) {
+            const int k = kb + 128 * s + kl;
+            const bool ok = k < d;   // d % 8 == 0: a lane's 8 columns are all in or all out
+            const uint32_t kbytes = (uint32_t)k * 2u;
+            st.g[s] = buf_load16(rg, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
+            st.u[s] = buf_load16(ru, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                st.x[s][g] = buf_load16(rx, ok && xoff[g] < x_bytes ? xoff[g] + kbytes : x_bytes, 0);
+        }
+    };
+    f32x4_t ag[NG], au[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) ag[g] = au[g] = zero4();
+    auto mma = [&](const GuStage<NG>& st) {
+#pragma unroll
+        for (int s = 0; s < kGuSteps; ++s)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                ag[g] = mfma16(st.g[s], st.x[s][g], ag[g]);
+                au[g] = mfma16(st.u[s], st.x[s][g], au[g]);
+            }
+    };
+
+    constexpr int KS = 128 * kGuSteps;   // columns per stage (all 4 waves)
+    GuStage<NG> s0, s1;
+    load(0, s0);
+    for (int kb = 0; kb < d; kb += 2 * KS) {
+        load(kb + KS, s1);
+        mma(s0);
+        settle_acc<NG>(ag);
+        settle_acc<NG>(au);
+        load(kb + 2 * KS, s0);
+        mma(s1);
+        settle_acc<NG>(ag);
+        settle_acc<NG>(au);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            red[w][g][0][i][l] = ag[g][i];
+            red[w][g][1][i][l] = au[g][i];
+        }
+    __syncthreads();
+    // wave w finishes token groups w, w + 4, ...: channel j0 + 4 q4 + i, token 16 g + r
+    for (int g = w; g < NG; g += 4) {
+        const int n = 16 * g + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int jc = j0 + 4 * q4 + i;
+            // channels past F (up to the block's end) get h = 0: the down
+            // projection reads h 8 channels at a time
+            if (n < a.B) {
+                float gg = 0.f, uu = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    gg += red[v][g][0][i][l];
+                    uu += red[v][g][1][i][l];
+                }
+                float hv = gg / (1.f + expf(-gg)) * uu;
+                if (jc >= a.F || !a.mask[(size_t)n * a.F + jc]) hv = 0.f;
+                const uint32_t hi = bf16_rne(hv);
+                const uint32_t lo = bf16_rne(hv - __uint_as_float(hi << 16));
+                a.hb[(size_t)n * a.f_pad + jc] = (uint16_t)hi;
+                a.hb[((size_t)a.B + n) * a.f_pad + jc] = (uint16_t)lo;
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// Down.  Block (cx, ks): columns 128 cx .. + 128 and channel slice ks (rows
+// [f0, f1), a multiple of 64 long), every token.  Rows go 64 at a time: each
+// thread loads 4 rows of one 8-column block of W_down and writes them to LDS
+// transposed, [column][row], so the B operand (one column, 8 rows per lane)
+// is a 16-byte LDS read.  Wave w owns columns 32 w .. + 32 (two N-tiles); the
+// A operand is h (hi, then lo) for 16 tokens x 8 channels, 16-byte loads from
+// the [B][f_pad] arrays.  Partial y of slice ks goes to ypart[token][ks][col].
+// ===========================================================================
+struct DnArgs {
+    const uint16_t* wd;     // [F][d]
+    const uint16_t* hb;     // [2][B][f_pad]
+    float* ypart;           // [B][KS][d]
+    int B, d, F, f_pad, KS, chunk;
+};
+
+constexpr int kDnCols = 128;
+constexpr int kDnRS = 72;
+
+template <int NG>
+struct DnStage {
+    uint4 w[4];             // rows 4p .. 4p + 3 of this thread's column block
+    uint4 h[2][NG][2];      // [K-step][token group][hi, lo]
+};
+
+template <int NG>
+__global__ void __launch_bounds__(256) k_down_batch(DnArgs a) {
+    constexpr int PD = NG <= 2 ? 4 : 2;        // stages in flight
+    constexpr int TILE = kDnCols * kDnRS;      // bf16 per LDS buffer
+    __shared__ uint4 lds_raw[2 * TILE / 8];
+    uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int r = l & 15, q4 = l >> 4;
+    const int c0 = blockIdx.x * kDnCols, ks = blockIdx.y;
+    const int f0 = ks * a.chunk, f1 = min(a.F, f0 + a.chunk);
+    const int d = a.d;
+    const uint32_t row_bytes = (uint32_t)d * 2u, w_bytes = (uint32_t)a.F * row_bytes;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wd, w_bytes);
+    const uint32_t h_bytes = 2u * (uint32_t)a.B * (uint32_t)a.f_pad * 2u;
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.hb, h_bytes);
+    // W loads: thread t -> column block cb (8 columns), rows 4p .. 4p + 3
+    const int cb = t & 15, p = t >> 4;
+    const bool col_ok = c0 + 8 * cb < d;   // d % 8 == 0
+    const uint32_t col_off = (uint32_t)(c0 + 8 * cb) * 2u;
+    uint32_t hrow[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int n = 16 * g + r;
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+            hrow[g][hl] = n < a.B ? ((uint32_t)hl * a.B + n) * (uint32_t)a.f_pad * 2u : h_bytes;
+    }
+
+    auto load_stage = [&](int s, DnStage<NG>& st) {
+        const int rb = f0 + 64 * s;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = rb + 4 * p + i;
+            st.w[i] = buf_load16(rw, (col_ok && row < f1) ? (uint32_t)row * row_bytes + col_off : w_bytes, 0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int row = rb + 32 * kk + 8 * q4;
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    st.h[kk][g][hl] =
+                        buf_load16(rh, (row < f1 && hrow[g][hl] < h_bytes) ? hrow[g][hl] + (uint32_t)row * 2u : h_bytes, 0);
+        }
+    };
+    // 8 columns x 4 rows -> [column][rows 4p .. 4p + 3] (8 bytes per column)
+    auto store_stage = [&](const DnStage<NG>& st, uint16_t* buf) {
+        const int chunk = (p >> 1) ^ (cb & 7), sub = 4 * (p & 1);
+        const uint32_t w0[4] = {st.w[0].x, st.w[0].y, st.w[0].z, st.w[0].w};
+        const uint32_t w1[4] = {st.w[1].x, st.w[1].y, st.w[1].z, st.w[1].w};
+        const uint32_t w2[4] = {st.w[2].x, st.w[2].y, st.w[2].z, st.w[2].w};
+        const uint32_t w3[4] = {st.w[3].x, st.w[3].y, st.w[3].z, st.w[3].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int wi = e / 2;
+            // the column's bf16 from rows 0/1 and 2/3 (low half = the lower row)
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t lo01 = __builtin_amdgcn_perm(w1[wi], w0[wi], sel);
+            const uint32_t lo23 = __builtin_amdgcn_perm(w3[wi], w2[wi], sel);
+            *reinterpret_cast<uint2*>(buf + (8 * cb + e) * kDnRS + 8 * chunk + sub) = make_uint2(lo01, lo23);
+        }
+    };
+    f32x4_t acc[2][NG];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[u][g] = zero4();
+    auto mma_stage = [&](const DnStage<NG>& st, const uint16_t* buf) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int col = 32 * w + 16 * u + r;
+                const int chunk = (4 * kk + q4) ^ ((col >> 3) & 7);
+                const uint4 bv = *reinterpret_cast<const uint4*>(buf + col * kDnRS + 8 * chunk);
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    acc[u][g] = mfma16(st.h[kk][g][0], bv, acc[u][g]);
+                    acc[u][g] = mfma16(st.h[kk][g][1], bv, acc[u][g]);
+                }
+            }
+        }
+    };
+
+    const int nst = (f1 - f0 + 63) / 64;
+    DnStage<NG> ring[PD];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load_stage(i, ring[i]);
+    for (int s0 = 0; s0 < nst; s0 += PD) {
+#pragma unroll
+        for (int i = 0; i < PD; ++i) {
+            uint16_t* buf = lds + (i & 1) * TILE;
+            store_stage(ring[i], buf);
+            lds_barrier();
+            mma_stage(ring[i], buf);
+            load_stage(s0 + i + PD, ring[i]);
+        }
+    }
+    // C[token 16 g + 4 q4 + i][column 32 w + 16 u + r]
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = c0 + 32 * w + 16 * u + r;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 16 * g + 4 * q4 + i;
+                if (n < a.B && c < d) a.ypart[((size_t)n * a.KS + ks) * d + c] = acc[u][g][i];
+            }
+    }
+}
+
+// Channel slices of the down projection: about 2 blocks per compute unit,
+// whole 64-row stages, at most what the partial-sum region holds.
+DnSplit down_batch_split(int B, int d, int F) {
+    const int cols = (d + kDnCols - 1) / kDnCols;
+    int ks = (512 + cols - 1) / cols;
+    const int stages = (F + 63) / 64;
+    if (ks > stages) ks = stages;
+    if (ks > stage2_blocks_max(B)) ks = stage2_blocks_max(B);
+    if (ks < 1) ks = 1;
+    DnSplit r;
+    r.chunk = (stages + ks - 1) / ks * 64;
+    r.KS = (F + r.chunk - 1) / r.chunk;
+    return r;
+}
+
+template <int NG>
+static hipError_t go_gateup_down(const GuArgs& gu, const DnArgs& dn, hipStream_t s) {
+    hipLaunchKernelGGL(k_gateup_batch<NG>, dim3((gu.F + 15) / 16), dim3(256), 0, s, gu);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_down_batch<NG>, dim3((dn.d + kDnCols - 1) / kDnCols, dn.KS), dim3(256), 0, s, dn);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage2_batch(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
+                               const uint16_t* wd, const uint8_t* mask, uint16_t* hb, int B, int d,
+                               int F, int f_pad, float* ypart, int* ks_out, hipStream_t s) {
+    const DnSplit sp = down_batch_split(B, d, F);
+    *ks_out = sp.KS;
+    GuArgs gu{x, wg_t, wu_t, mask, hb, B, d, F, f_pad};
+    DnArgs dn{wd, hb, ypart, B, d, F, f_pad, sp.KS, sp.chunk};
+    const int ng = (B + 15) / 16;
+    if (ng == 1) return go_gateup_down<1>(gu, dn, s);
+    if (ng == 2) return go_gateup_down<2>(gu, dn, s);
+    if (ng == 3) return go_gateup_down<3>(gu, dn, s);
+    return go_gateup_down<4>(gu, dn, s);
+}
+
+}  // namespace prox

@@ -68,12 +68,29 @@ inline S1Geom s1_geom(int k_in, int F, int kind, int batch, int n_cu) {
     return g;
 }
 
-// Workspace carve-up (byte offsets) for one (d, F, B, kind).
+// Batches of at least this many tokens take the matrix-core path.
+constexpr int kBatchMin = 8;
+
+// Row splits of the batched proxy GEMM (rows per split: whole 128-row groups).
+struct PbSplit {
+    int ks1, rps;
+};
+PbSplit proxy_batch_split(int d, int F, int kind);
+// Channel slices of the batched down projection (chunk: rows per slice).
+struct DnSplit {
+    int KS, chunk;
+};
+DnSplit down_batch_split(int B, int d, int F);
+
+// Workspace carve-up (byte offsets) for one (d, F, B, kind).  The batch
+// regions (xm, bpart, bmask, hb) are empty below kBatchMin tokens.
 struct WsLayout {
-    size_t key, ypart, gh, part, tcnt, total;
+    size_t key, ypart, gh, part, tcnt, xm, bpart, bmask, hb, total;
 };
 inline WsLayout ws_layout(int d, int F, int B, int kind) {
     const int fp = f_pad_of(F, kind);
+    const bool batch = B >= kBatchMin;
+    const size_t ks1 = batch ? (size_t)proxy_batch_split(d, F, kind).ks1 : 0;
     WsLayout L;
     size_t o = 0;
     L.key = o;    o = align_up(o + (size_t)B * fp * 4, 256);
@@ -81,6 +98,10 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
     L.gh = o;     o = align_up(o + (size_t)B * kGhBins * 4, 256);
     L.part = o;   o = align_up(o + (size_t)B * (fp / tile_channels(kind) + s1_blocks_max(B)) * 2 * kPartChannels * 8, 256);
     L.tcnt = o;   o = align_up(o + (size_t)B * (fp / tile_channels(kind)) * 8, 256);
+    L.xm = o;     o = align_up(o + (batch ? (size_t)B * d * 2 : 0), 256);
+    L.bpart = o;  o = align_up(o + (ks1 > 1 ? ks1 * 2 * B * fp * 4 : 0), 256);
+    L.bmask = o;  o = align_up(o + (batch ? (size_t)B * F : 0), 256);
+    L.hb = o;     o = align_up(o + (batch ? (size_t)2 * B * fp * 2 : 0), 256);
     L.total = o;
     return L;
 }
@@ -98,5 +119,19 @@ hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t
                          float* ypart, hipStream_t s);
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, uint32_t* gh,
                            hipStream_t s);
+// Stage-2 selection only: mask (required) and idx (nullable) from the keys.
+hipError_t launch_select(const float* key, const uint32_t* gh, int B, int d, int F, int f_pad, int k_ff,
+                         int W2, int32_t* idx, uint8_t* mask, hipStream_t s);
+
+// ---- batch launchers (prox_batch.hip)
+hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,
+                       hipStream_t s);
+hipError_t launch_proxy_batch(const uint16_t* xm, int B, int d, const ProxyView& p, float* part,
+                              unsigned long long* tcnt, uint32_t gen, float* key, uint32_t* gh,
+                              double* h_tap, float* key_tap, hipStream_t s);
+// Gate/up and down over the tokens' masks; *ks_out = partial slices in ypart.
+hipError_t launch_stage2_batch(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
+                               const uint16_t* wd, const uint8_t* mask, uint16_t* hb, int B, int d,
+                               int F, int f_pad, float* ypart, int* ks_out, hipStream_t s);
 
 }  // namespace prox

@@ -562,6 +562,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
             if (t < 2 * TC)
                 __hip_atomic_store(&slot[((size_t)2 * wb + t / TC) * kPartChannels + t % TC], v,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
             __syncthreads();
             if (t == 0) sc[22] = s1_arrive(a.tcnt + (size_t)b * a.tiles + tile, a.gen, w1 - w0 + 1);
             lds_barrier();
@@ -760,7 +761,7 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
 constexpr int kSmallCand = 128;   // candidates ranked by direct comparison up to this many
 constexpr int kCandCap = 1024;    // candidates listed in LDS (more: the slow path)
 
-template <int PK, int R, int G>
+template <int PK, int R, int G, bool STREAM>
 __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     constexpr int NT = kS2Threads;
     constexpr int NW = NT / kWave;
@@ -792,7 +793,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         const int col = r * 4096 + t * 8;
         voff[r] = col < a.d ? (uint32_t)col * 2u : mat_bytes;   // past d: read as zeros
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (col < a.d) v = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
+        if (STREAM && col < a.d) v = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
         xr[r][0] = bf16_lo(v.x); xr[r][1] = bf16_hi(v.x);
         xr[r][2] = bf16_lo(v.y); xr[r][3] = bf16_hi(v.y);
         xr[r][4] = bf16_lo(v.z); xr[r][5] = bf16_hi(v.z);
@@ -816,7 +817,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     }
     // the first NT channels of the range, one per thread
     const uint32_t own0 = t < L ? __float_as_uint(keyb[r0 + t]) : 0u;
-    if (t == 0) chan[0] = 0;                               // row 0 stands in for an empty list
+    if (STREAM && t == 0) chan[0] = 0;                     // row 0 stands in for an empty list
 
     // ---- threshold bin
     const bool all = k >= F, none = k == 0;
@@ -865,7 +866,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             while (m) {
                 const int q = __builtin_ctzll(m);
                 m &= m - 1;
-                if (cr >= c0 && cr < c1) chan[cr - c0] = (uint16_t)(t * PK + q);
+                if (STREAM && cr >= c0 && cr < c1) chan[cr - c0] = (uint16_t)(t * PK + q);
                 ++cr;
             }
         }
@@ -889,7 +890,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int cert_before = sc[18];                        // certain keys before the range
     const int E = min(nc, G);
     RowGroup<R, G> cur, nxt;
-    load_group<R, G>(rs, chan, 0, E, row_bytes, mat_bytes, voff, cur);
+    if constexpr (STREAM) load_group<R, G>(rs, chan, 0, E, row_bytes, mat_bytes, voff, cur);
 
     int nks = 0, kc_before = 0;
     if (listed) {
@@ -961,7 +962,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         nks = s1 - s0;
         for (int i = t; i < ncand; i += NT) {
             const int r = kr[i];
-            if ((cidx[i] & 0x8000u) && r >= s0 && r < s1) chan[nc + r - s0] = cidx[i] & 0x7fffu;
+            if (STREAM && (cidx[i] & 0x8000u) && r >= s0 && r < s1) chan[nc + r - s0] = cidx[i] & 0x7fffu;
         }
     } else {
         // ---- slow path (more candidates than the list holds): the exact
@@ -988,7 +989,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         for (int q = 0; q < PK; ++q) {
             const bool e = kb[q] == T;
             const bool on = ((int)kb[q] >= 0 && kb[q] > T) || (e && eb < need);
-            if (on && pos >= k0 && pos < k1) chan[pos - k0] = (uint16_t)(t * PK + q);
+            if (STREAM && on && pos >= k0 && pos < k1) chan[pos - k0] = (uint16_t)(t * PK + q);
             const int j = t * PK + q;
             if (j >= r0 && j < r1) {
                 if (on && a.idx) a.idx[(size_t)b * k + pos] = j;
@@ -1023,6 +1024,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     }
     const int n = nc + nks;
     lds_barrier();
+    if constexpr (!STREAM) return;   // selection only: mask and idx are written
 
     // ---- sparse SwiGLU: group 0 = entries [0, E), then [E, n) G at a time.
     // The loads are unconditional and the loop has no exit from its middle:
@@ -1055,12 +1057,13 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     }
 }
 
-template <int PK, int R, int G>
+template <int PK, int R, int G, bool STREAM>
 static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
-    const int cap = (a.k + a.W2 - 1) / a.W2 + 2;          // list length bound: ceil(C/W2) + ceil(KC/W2)
+    // list length bound: ceil(C/W2) + ceil(KC/W2); selection only keeps no list
+    const int cap = STREAM ? (a.k + a.W2 - 1) / a.W2 + 2 : 0;
     const size_t dyn = ((size_t)(a.F + 64 + 3) & ~(size_t)3) * 4 + ((size_t)kCandCap + 64) * 4 +
                        ((size_t)kCandCap * 2 + 64 + cap + 64) * 2;
-    auto fn = k_stage2<PK, R, G>;
+    auto fn = k_stage2<PK, R, G, STREAM>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -1069,18 +1072,18 @@ static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int R, int G>
+template <int R, int G, bool STREAM>
 static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
     const int per = (a.F + kS2Threads - 1) / kS2Threads;
-    if (per <= 4) return go_stage2<4, R, G>(a, B, s);
-    if (per <= 8) return go_stage2<8, R, G>(a, B, s);
-    if (per <= 16) return go_stage2<16, R, G>(a, B, s);
-    if (per <= 24) return go_stage2<24, R, G>(a, B, s);
-    if (per <= 32) return go_stage2<32, R, G>(a, B, s);
-    if (per <= 40) return go_stage2<40, R, G>(a, B, s);
-    if (per <= 48) return go_stage2<48, R, G>(a, B, s);
-    if (per <= 56) return go_stage2<56, R, G>(a, B, s);
-    return go_stage2<64, R, G>(a, B, s);
+    if (per <= 4) return go_stage2<4, R, G, STREAM>(a, B, s);
+    if (per <= 8) return go_stage2<8, R, G, STREAM>(a, B, s);
+    if (per <= 16) return go_stage2<16, R, G, STREAM>(a, B, s);
+    if (per <= 24) return go_stage2<24, R, G, STREAM>(a, B, s);
+    if (per <= 32) return go_stage2<32, R, G, STREAM>(a, B, s);
+    if (per <= 40) return go_stage2<40, R, G, STREAM>(a, B, s);
+    if (per <= 48) return go_stage2<48, R, G, STREAM>(a, B, s);
+    if (per <= 56) return go_stage2<56, R, G, STREAM>(a, B, s);
+    return go_stage2<64, R, G, STREAM>(a, B, s);
 }
 
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
@@ -1088,27 +1091,33 @@ hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t
                          int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask,
                          float* ypart, hipStream_t s) {
     Stage2Args a{x, wg_t, wu_t, wd, key, gh, d, F, f_pad, k_ff, W2, idx, mask, ypart};
-    if (d <= 4096) return stage2_pk<1, 4>(a, B, s);
-    if (d <= 8192) return stage2_pk<2, 2>(a, B, s);
-    return stage2_pk<4, 1>(a, B, s);
+    if (d <= 4096) return stage2_pk<1, 4, true>(a, B, s);
+    if (d <= 8192) return stage2_pk<2, 2, true>(a, B, s);
+    return stage2_pk<4, 1, true>(a, B, s);
+}
+
+hipError_t launch_select(const float* key, const uint32_t* gh, int B, int d, int F, int f_pad, int k_ff,
+                         int W2, int32_t* idx, uint8_t* mask, hipStream_t s) {
+    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, gh, d, F, f_pad, k_ff, W2, idx, mask, nullptr};
+    return stage2_pk<1, 1, false>(a, B, s);
 }
 
 // ---------------------------------------------------------------------------
 // y = sum of the W2 block partials, fixed order, and the token's key
-// histogram back to zero for the next call.  grid (ceil(d / 32), B), block
-// 256: thread (g = t / 8, c = t % 8) sums partials g, g + 32, ... of columns
-// 4c .. 4c + 3 of the block's 32 (all of its loads in flight at once), then
-// the 32 groups are combined in LDS in a fixed tree.
+// histogram back to zero for the next call.  grid (ceil(d / 16), B), block
+// 256: thread (g = t / 4, c = t % 4) sums partials g, g + 64, ... of columns
+// 4c .. 4c + 3 of the block's 16 (all of its loads in flight at once), then
+// the 64 groups are combined in LDS in a fixed tree.
 // ---------------------------------------------------------------------------
-constexpr int kRedCols = 32;
-constexpr int kRedGroups = 32;
+constexpr int kRedCols = 16;
+constexpr int kRedGroups = 64;
 constexpr int kRedMax = kMaxW2Total / kRedGroups;   // partials per thread
 
 __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypart, int d, int W2,
                                                   float* __restrict__ y, uint32_t* __restrict__ gh) {
     __shared__ float4 acc[kRedGroups][kRedCols / 4];
     const int b = blockIdx.y, t = threadIdx.x;
-    const int g = t >> 3, c = t & 7;
+    const int g = t >> 2, c = t & 3;
     const int col = blockIdx.x * kRedCols + 4 * c;
     const bool in = col < d;                       // d % 8 == 0, so a quad is all in or all out
     const float* src = ypart + (size_t)b * W2 * d + (in ? col : 0);
