@@ -202,8 +202,9 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
         uint16_t* hb = reinterpret_cast<uint16_t*>(ws + L.hb);
         e = launch_xsel(xb, batch, d, k_in, xm, taps ? taps->in_idx : nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "input selection");
+        // (no key histogram here: the selection ranks each token's keys itself)
         e = launch_proxy_batch(xm, batch, d, pv, reinterpret_cast<float*>(ws + L.bpart), tcnt, next_call_tag(),
-                               key, gh, taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr, s);
+                               key, taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "proxy GEMM");
         if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
         e = launch_select(key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, bmask, s);

@@ -41,14 +41,6 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
-// Keeps a value in registers at this point of the program (no code emitted):
-// stops the compiler from sinking the accumulation below the next loads.
-template <int N>
-__device__ __forceinline__ void settle_acc(f32x4_t (&v)[N]) {
-#pragma unroll
-    for (int g = 0; g < N; ++g) asm volatile("" : "+v"(v[g]) : : "memory");
-}
-
 // Round to nearest even, finite inputs.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -64,16 +56,33 @@ __device__ __forceinline__ uint32_t pair_bf16(int qa, int qb) {
 // ===========================================================================
 // Input selection: one block per token.  Thread t holds x[16t .. 16t + 15].
 // Keys are |x| as bf16 bits (sign cleared), so the order of keys is the order
-// of magnitudes; T = the k-th largest key, all keys above T are kept and the
-// keys equal to T are kept in index order until k are kept.
+// of magnitudes.  T = the k-th largest key is found bit by bit from the top
+// (the largest value with at least k keys >= it), each bit one block count;
+// keys above T are kept and keys equal to T are kept in index order until k
+// are kept.
 // ===========================================================================
-constexpr int kXselThreads = 1024;
-constexpr int kXselPer = 16;   // d <= 16384
+constexpr int kXselPer = 16;   // keys per thread; blocks of d / 16 threads (d <= 16384)
 
-__global__ void __launch_bounds__(kXselThreads) k_xsel(const uint16_t* __restrict__ x, int d, int k,
+// Number of (valid) keys >= v over the block; `slot` = NT / 64 ints of LDS
+// not in use by the previous call (callers alternate two slot sets).
+template <int NT>
+__device__ __forceinline__ int xsel_count_ge(const uint32_t (&key)[kXselPer], const bool (&valid)[kXselPer],
+                                             uint32_t v, int* slot) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kXselPer; ++q) c += __popcll(__ballot(valid[q] && key[q] >= v));
+    if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = c;
+    lds_barrier();
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) tot += slot[i];
+    return tot;
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) k_xsel(const uint16_t* __restrict__ x, int d, int k,
                                                       uint16_t* __restrict__ xm, int32_t* __restrict__ in_idx) {
-    __shared__ uint32_t hist[2049];
-    __shared__ int sc[32];
+    __shared__ int sc[2][32];
     const int b = blockIdx.x, t = threadIdx.x;
     uint32_t v[kXselPer], key[kXselPer];
     bool valid[kXselPer];
@@ -85,31 +94,19 @@ __global__ void __launch_bounds__(kXselThreads) k_xsel(const uint16_t* __restric
     uint32_t T = 0;
     int cgt = 0;
     if (!all && !none) {
-        SelectState st = block_coarse_bin<kXselPer, kXselThreads>(key, valid, k, 15, hist, sc);
-        if (st.shift > 0) {
-            const int nb = 1 << st.shift;
-            for (int i = t; i < nb; i += kXselThreads) hist[i] = 0u;
-            lds_barrier();
-#pragma unroll
-            for (int q = 0; q < kXselPer; ++q)
-                if (valid[q] && (key[q] >> st.shift) == st.prefix) atomicAdd(&hist[key[q] & (nb - 1)], 1u);
-            lds_barrier();
-            uint32_t digit;
-            int ab;
-            find_bin<kXselThreads>(hist, nb, st.krem, sc, digit, ab);
-            T = (st.prefix << st.shift) | digit;
-            cgt = st.above + ab;
-        } else {
-            T = st.prefix;
-            cgt = st.above;
+        int round = 0;
+        for (int bit = 14; bit >= 0; --bit, ++round) {
+            const uint32_t cand = T | (1u << bit);
+            if (xsel_count_ge<NT>(key, valid, cand, sc[round & 1]) >= k) T = cand;
         }
+        cgt = xsel_count_ge<NT>(key, valid, T + 1u, sc[round & 1]);   // round 15: the other slot set
     }
     const int need = k - cgt;   // keys equal to T that are kept, lowest indices first
     int neq = 0;
 #pragma unroll
     for (int q = 0; q < kXselPer; ++q) neq += (valid[q] && key[q] == T) ? 1 : 0;
     int tot;
-    int eq_before = block_excl_scan<kXselThreads>(neq, sc, tot);
+    int eq_before = block_excl_scan<NT>(neq, sc[0], tot);
     bool keep[kXselPer];
     int nk = 0;
 #pragma unroll
@@ -119,7 +116,7 @@ __global__ void __launch_bounds__(kXselThreads) k_xsel(const uint16_t* __restric
         eq_before += eq ? 1 : 0;
         nk += keep[q] ? 1 : 0;
     }
-    int pos = block_excl_scan<kXselThreads>(nk, sc, tot);
+    int pos = block_excl_scan<NT>(nk, sc[1], tot);
     const int base = t * kXselPer;
 #pragma unroll
     for (int q = 0; q < kXselPer; q += 8) {
@@ -140,23 +137,26 @@ __global__ void __launch_bounds__(kXselThreads) k_xsel(const uint16_t* __restric
 
 hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,
                        hipStream_t s) {
-    hipLaunchKernelGGL(k_xsel, dim3(B), dim3(kXselThreads), 0, s, x, d, k_in, xm, in_idx);
+    const int per_block = (d + kXselPer - 1) / kXselPer;
+    if (per_block <= 256) hipLaunchKernelGGL(k_xsel<256>, dim3(B), dim3(256), 0, s, x, d, k_in, xm, in_idx);
+    else if (per_block <= 512) hipLaunchKernelGGL(k_xsel<512>, dim3(B), dim3(512), 0, s, x, d, k_in, xm, in_idx);
+    else hipLaunchKernelGGL(k_xsel<1024>, dim3(B), dim3(1024), 0, s, x, d, k_in, xm, in_idx);
     return hipGetLastError();
 }
 
 // ===========================================================================
 // Proxy GEMM.  Block (tile, split): the tile's TC channels (64 int8 / 128
-// int4) over rows [r0, r1) of the split, every token.  Rows go 64 at a time
-// ("stages"): each thread loads two rows of one 16-byte column block of the
-// tile, turns its codes into bf16 and writes them to LDS transposed,
-// [mat][channel][row]; the MFMA A operand (16 channels x 8 rows per lane) is
-// then one 16-byte LDS read.  B is x~ (token-major, rows contiguous), read
-// from global memory.  Wave w owns M-tiles (16 channels) w*MT/4 .. of both
-// matrices, so each lane ends with gate and up of the same channels.
-//
-// LDS rows are 72 bf16 (64 + 8 padding) and the 16-byte chunks of a channel
-// row are permuted by (chunk ^ column block), which spreads both the
-// transposing writes and the operand reads over the banks.
+// int4) over rows [r0, r1) of the split, every token.  Wave w owns M-tile w
+// (channels 16w .. 16w + 15 of the tile, gate and up) and works on its own:
+// rows go 128 at a time ("stages"), lane l loads rows 2l and 2l + 1 of the
+// wave's columns (int4: one 16-byte column block, int8: two), turns the codes
+// into bf16 and writes them to the wave's LDS region transposed,
+// [mat][channel][row], one dword (two rows) per write; the MFMA A operand (16
+// channels x 8 rows per lane) is then one 16-byte LDS read.  A wave's LDS
+// operations complete in order, so no barrier separates the writes from the
+// reads.  B is x~ (token-major, rows contiguous), read from global memory.
+// A stage is one 128-row group: its fp32 sums go to fp64 after the stage
+// (int4: times the group's scales, which travel with the stage's loads).
 // ===========================================================================
 struct PbArgs {
     const uint16_t* xm;       // [B][d] x~
@@ -167,52 +167,47 @@ struct PbArgs {
     unsigned long long* tcnt; // [tiles] arrival counters
     uint32_t gen;
     float* key;               // [B][f_pad]
-    uint32_t* gh;             // [B][kGhBins]
     double* h_tap;            // [B][F] or null
     float* key_tap;           // [B][F] or null
 };
 
-constexpr int kPbRS = 72;     // LDS row stride of the transposed tiles, in bf16
-constexpr int kPbDepth = 4;   // stages in flight per thread
+constexpr int kPbRS = 136;    // LDS row stride of a transposed channel, in bf16 (128 + 8)
+constexpr int kPbWave = 2 * 16 * kPbRS;   // bf16 per wave region
 
-template <int NG>
+template <int KIND, int NG>
 struct PbStage {
-    uint4 c[2];         // rows 2p, 2p + 1 of this thread's column block
-    uint4 x[2][NG];     // B operands of the stage's two K-steps
+    uint4 c[KIND == 1 ? 4 : 2];   // rows 2l, 2l + 1 (int8: two column blocks each)
+    uint4 x[4][NG];               // B operands of the stage's four K-steps
+    float4 sg, su;                // int4: the group's scales of this lane's channels
 };
 
 __device__ __forceinline__ void pb_score(const PbArgs& a, int b, int j, double g, double u) {
     const double h = g / (1.0 + exp(-g)) * u;
     const float kf = (float)fabs(h);
     a.key[(size_t)b * a.f_pad + j] = kf;
-    __hip_atomic_fetch_add(a.gh + (size_t)b * kGhBins + (__float_as_uint(kf) >> kGhShift), 1u,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.h_tap) a.h_tap[(size_t)b * a.F + j] = h;
     if (a.key_tap) a.key_tap[(size_t)b * a.F + j] = kf;
 }
 
-template <int KIND, int NG>
-__global__ void __launch_bounds__(256) k_proxy_batch(PbArgs a) {
+template <int KIND, int NG, int PD>
+__global__ void __launch_bounds__(KIND == 1 ? 256 : 512) k_proxy_batch(PbArgs a) {
     constexpr int TC = KIND == 1 ? 64 : 128;   // channels of a tile
-    constexpr int CPB = TC / 8;                // channels per 16-byte column block (per matrix)
-    constexpr int MT = TC / 16;                // M-tiles per matrix
-    constexpr int MW = MT / 4;                 // M-tiles per wave
-    constexpr int TILE = 2 * TC * kPbRS;       // bf16 per LDS buffer
-    __shared__ uint4 lds_raw[2 * TILE / 8];
+    constexpr int NW = TC / 16;                // waves (M-tiles)
+    extern __shared__ uint4 pb_dyn[];
     __shared__ int flag;
-    uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
 
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int r = l & 15, q4 = l >> 4;
+    uint16_t* buf = reinterpret_cast<uint16_t*>(pb_dyn) + w * kPbWave;
     const int tile = blockIdx.x / a.ks1, split = blockIdx.x % a.ks1;
     const int d = a.d;
     const int r0 = split * a.rps, r1 = min(d, r0 + a.rps);
+    const int ch0 = tile * TC + 16 * w;        // this wave's first channel
 
-    // loads: thread t -> column block cb, rows 2p, 2p + 1 of each stage
-    const int cb = t & 7, p = t >> 3;
     const uint32_t codes_bytes = (uint32_t)a.tiles * (uint32_t)d * kTileRowBytes;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.codes, codes_bytes);
     const uint32_t tile_off = (uint32_t)tile * (uint32_t)d * kTileRowBytes;
+    const uint32_t col_off = KIND == 1 ? 32u * w : 16u * w;
     const uint32_t x_bytes = (uint32_t)a.B * (uint32_t)d * 2u;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xm, x_bytes);
     uint32_t xrow[NG];   // byte offset of this lane's B-operand token row, or past the end
@@ -221,131 +216,135 @@ __global__ void __launch_bounds__(256) k_proxy_batch(PbArgs a) {
         const int n = 16 * g + r;
         xrow[g] = n < a.B ? (uint32_t)n * (uint32_t)d * 2u : x_bytes;
     }
+    const float* sg_base = a.scales + ch0 + 4 * q4;
+    const float* su_base = sg_base + (size_t)a.groups * a.f_pad;
 
-    auto load_stage = [&](int s, PbStage<NG>& st) {
-        const int ra = r0 + 64 * s + 2 * p;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = ra + h;
-            st.c[h] = buf_load16(rc, row < r1 ? (uint32_t)row * kTileRowBytes + cb * 16u : codes_bytes, tile_off);
+    auto load_stage = [&](int s, PbStage<KIND, NG>& st) {
+        const int rb = r0 + 128 * s;
+        if (KIND == 2) {
+            const int gi = min(rb / 128, a.groups - 1);
+            st.sg = *reinterpret_cast<const float4*>(sg_base + (size_t)gi * a.f_pad);
+            st.su = *reinterpret_cast<const float4*>(su_base + (size_t)gi * a.f_pad);
         }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int row = r0 + 64 * s + 32 * ks + 8 * q4;
+        for (int h = 0; h < 2; ++h) {
+            const int row = rb + 2 * l + h;
+            const uint32_t off = row < r1 ? (uint32_t)row * kTileRowBytes + col_off : codes_bytes;
+            if (KIND == 1) {
+                st.c[2 * h] = buf_load16(rc, off, tile_off);
+                st.c[2 * h + 1] = buf_load16(rc, row < r1 ? off + 16u : codes_bytes, tile_off);
+            } else {
+                st.c[h] = buf_load16(rc, off, tile_off);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int row = rb + 32 * ks + 8 * q4;
 #pragma unroll
             for (int g = 0; g < NG; ++g)
                 st.x[ks][g] = buf_load16(rx, (row < r1 && xrow[g] < x_bytes) ? xrow[g] + (uint32_t)row * 2u : x_bytes, 0);
         }
     };
 
-    // codes of rows 2p, 2p + 1 -> bf16 pairs at [mat][channel][rows 2p, 2p + 1]
-    auto store_stage = [&](const PbStage<NG>& st, uint16_t* buf) {
-        const uint32_t ca[4] = {st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w};
-        const uint32_t cbv[4] = {st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w};
-        const int chunk = (p >> 2) ^ cb, sub = 2 * (p & 3);
-#pragma unroll
-        for (int mat = 0; mat < 2; ++mat) {
-#pragma unroll
-            for (int e = 0; e < CPB; ++e) {
-                int qa, qb;
-                if (KIND == 1) {
-                    qa = __builtin_amdgcn_sbfe((int)ca[2 * mat + e / 4], 8 * (e % 4), 8);
-                    qb = __builtin_amdgcn_sbfe((int)cbv[2 * mat + e / 4], 8 * (e % 4), 8);
-                } else {
-                    qa = __builtin_amdgcn_sbfe((int)ca[2 * mat + e / 8], 4 * (e % 8), 4);
-                    qb = __builtin_amdgcn_sbfe((int)cbv[2 * mat + e / 8], 4 * (e % 8), 4);
-                }
-                const int ch = CPB * cb + e;
-                *reinterpret_cast<uint32_t*>(buf + (mat * TC + ch) * kPbRS + 8 * chunk + sub) = pair_bf16(qa, qb);
-            }
+    // code of channel c (0..15) of matrix mat in row h (0: row 2l, 1: row 2l + 1)
+    auto code = [&](const PbStage<KIND, NG>& st, int h, int mat, int c) -> int {
+        if (KIND == 1) {
+            const uint4 v = st.c[2 * h + c / 8];
+            const uint32_t wd = (mat == 0 ? ((c & 7) < 4 ? v.x : v.y) : ((c & 7) < 4 ? v.z : v.w));
+            return __builtin_amdgcn_sbfe((int)wd, 8 * (c % 4), 8);
+        } else {
+            const uint4 v = st.c[h];
+            const uint32_t wd = (mat == 0 ? (c < 8 ? v.x : v.y) : (c < 8 ? v.z : v.w));
+            return __builtin_amdgcn_sbfe((int)wd, 4 * (c % 8), 4);
         }
     };
-
-    f32x4_t acc[2 * MW][NG];   // [mat * MW + tile of the wave][token group]
-    double dacc[2 * MW][NG][4];
+    // rows 2l, 2l + 1 of every channel -> one dword at [mat][channel][2l]
+    auto store_stage = [&](const PbStage<KIND, NG>& st) {
 #pragma unroll
-    for (int c = 0; c < 2 * MW; ++c)
+        for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                *reinterpret_cast<uint32_t*>(buf + (mat * 16 + c) * kPbRS + 2 * l) =
+                    pair_bf16(code(st, 0, mat, c), code(st, 1, mat, c));
+    };
+
+    f32x4_t acc[2][NG];
+    double dacc[2][NG][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-            acc[c][g] = zero4();
+            acc[m][g] = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dacc[c][g][i] = 0.0;
+            for (int i = 0; i < 4; ++i) dacc[m][g][i] = 0.0;
         }
 
-    auto mma_stage = [&](const PbStage<NG>& st, const uint16_t* buf) {
+    auto mma_stage = [&](const PbStage<KIND, NG>& st) {
+        uint4 av[4][2];   // every A operand of the stage first, then the products
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int c = 0; c < 2 * MW; ++c) {
-                const int mat = c / MW, mt = w * MW + c % MW;
-                const int ch = 16 * mt + r;
-                const int chunk = (4 * ks + q4) ^ ((ch / CPB) & 7);
-                const uint4 av = *reinterpret_cast<const uint4*>(buf + (mat * TC + ch) * kPbRS + 8 * chunk);
+            for (int m = 0; m < 2; ++m)
+                av[ks][m] = *reinterpret_cast<const uint4*>(buf + (m * 16 + r) * kPbRS + 32 * ks + 8 * q4);
 #pragma unroll
-                for (int g = 0; g < NG; ++g) acc[c][g] = mfma16(av, st.x[ks][g], acc[c][g]);
-            }
-        }
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) acc[m][g] = mfma16(av[ks][m], st.x[ks][g], acc[m][g]);
     };
 
-    // every 128 rows: fp32 sums -> fp64 (int4: times the group's scales)
-    auto flush = [&](int grp) {
+    auto flush = [&](const PbStage<KIND, NG>& st) {
+        const float s4[2][4] = {{st.sg.x, st.sg.y, st.sg.z, st.sg.w}, {st.su.x, st.su.y, st.su.z, st.su.w}};
 #pragma unroll
-        for (int c = 0; c < 2 * MW; ++c) {
-            const int mat = c / MW, mt = w * MW + c % MW;
-            float4 sv = make_float4(1.f, 1.f, 1.f, 1.f);
-            if (KIND == 2) {
-                const int gi = min(grp, a.groups - 1);
-                sv = *reinterpret_cast<const float4*>(a.scales + ((size_t)mat * a.groups + gi) * a.f_pad +
-                                                     tile * TC + 16 * mt + 4 * q4);
-            }
-            const float s4[4] = {sv.x, sv.y, sv.z, sv.w};
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dacc[c][g][i] += KIND == 2 ? (double)acc[c][g][i] * (double)s4[i] : (double)acc[c][g][i];
-                acc[c][g] = zero4();
+                    dacc[m][g][i] += KIND == 2 ? (double)acc[m][g][i] * (double)s4[m][i] : (double)acc[m][g][i];
+                acc[m][g] = zero4();
             }
-        }
     };
 
-    const int nst = (r1 - r0 + 63) / 64;
-    PbStage<NG> ring[kPbDepth];
+    const int nst = (r1 - r0 + 127) / 128;
+    PbStage<KIND, NG> ring[PD];
 #pragma unroll
-    for (int i = 0; i < kPbDepth; ++i) load_stage(i, ring[i]);
-    // stages past nst read zeros (past r1), so the loop runs whole rounds of
-    // kPbDepth stages with unconditional loads
-    for (int s0 = 0; s0 < nst; s0 += kPbDepth) {
+    for (int i = 0; i < PD; ++i) {
+        load_stage(i, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);   // issue order = consumption order
+    }
+    // whole rounds of PD stages; stages past the split read zeros
+    for (int s0 = 0; s0 < nst; s0 += PD) {
 #pragma unroll
-        for (int i = 0; i < kPbDepth; ++i) {
-            uint16_t* buf = lds + (i & 1) * TILE;
-            store_stage(ring[i], buf);
-            lds_barrier();
-            mma_stage(ring[i], buf);
-            load_stage(s0 + i + kPbDepth, ring[i]);
-            if (i & 1) flush((r0 + 64 * (s0 + i)) / 128);
+        for (int i = 0; i < PD; ++i) {
+            store_stage(ring[i]);
+            asm volatile("" ::: "memory");   // the LDS reads below follow the writes
+            mma_stage(ring[i]);
+            flush(ring[i]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_stage(s0 + i + PD, ring[i]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // this lane: gate / up of channels 16 mt + 4 q4 + i, tokens 16 g + r
+    // this lane: gate / up of channels ch0 + 4 q4 + i, tokens 16 g + r
     if (a.ks1 > 1) {
         // publish this split's sums; the block that completes the tile adds the
         // splits in order (device-scope stores and loads, coherent across the
         // chip's L2 caches; the stores complete before the arrival is counted)
 #pragma unroll
-        for (int c = 0; c < 2 * MW; ++c) {
-            const int mat = c / MW, mt = w * MW + c % MW;
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int n = 16 * g + r;
                 if (n < a.B) {
-                    float* dst = a.part + (((size_t)split * 2 + mat) * a.B + n) * a.f_pad + tile * TC + 16 * mt + 4 * q4;
+                    float* dst = a.part + (((size_t)split * 2 + m) * a.B + n) * a.f_pad + ch0 + 4 * q4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        __hip_atomic_store(dst + i, (float)dacc[c][g][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(dst + i, (float)dacc[m][g][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
-        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
         __syncthreads();
         if (t == 0) {
@@ -361,11 +360,10 @@ __global__ void __launch_bounds__(256) k_proxy_batch(PbArgs a) {
                 }
             }
         }
-        lds_barrier();
+        __syncthreads();
         if (!flag) return;
 #pragma unroll
-        for (int c = 0; c < 2 * MW; ++c) {
-            const int mat = c / MW, mt = w * MW + c % MW;
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int n = 16 * g + r;
@@ -375,46 +373,41 @@ __global__ void __launch_bounds__(256) k_proxy_batch(PbArgs a) {
                         double sum = 0.0;
                         for (int sp = 0; sp < a.ks1; ++sp)
                             sum += (double)__hip_atomic_load(
-                                a.part + (((size_t)sp * 2 + mat) * a.B + n) * a.f_pad + tile * TC + 16 * mt + 4 * q4 + i,
+                                a.part + (((size_t)sp * 2 + m) * a.B + n) * a.f_pad + ch0 + 4 * q4 + i,
                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        dacc[c][g][i] = sum;
+                        dacc[m][g][i] = sum;
                     }
                 }
             }
-        }
     }
-    // scores: c < MW are gate tiles, c + MW the up tiles of the same channels
 #pragma unroll
-    for (int c = 0; c < MW; ++c) {
-        const int mt = w * MW + c;
+    for (int i = 0; i < 4; ++i) {
+        const int j = ch0 + 4 * q4 + i;
+        if (j >= a.F) continue;
+        double sg = 1.0, su = 1.0;
+        if (KIND == 1) {
+            sg = (double)a.scales[j];
+            su = (double)a.scales[a.f_pad + j];
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = tile * TC + 16 * mt + 4 * q4 + i;
-            if (j >= a.F) continue;
-            double sg = 1.0, su = 1.0;
-            if (KIND == 1) {
-                sg = (double)a.scales[j];
-                su = (double)a.scales[a.f_pad + j];
-            }
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int n = 16 * g + r;
-                if (n < a.B) pb_score(a, n, j, dacc[c][g][i] * sg, dacc[c + MW][g][i] * su);
-            }
+        for (int g = 0; g < NG; ++g) {
+            const int n = 16 * g + r;
+            if (n < a.B) pb_score(a, n, j, dacc[0][g][i] * sg, dacc[1][g][i] * su);
         }
     }
 }
 
-// Row splits of the proxy GEMM: enough blocks to cover the chip about once
-// (tiles * splits >= kPbBlocks), splits of whole 128-row groups, at most
+// Row splits of the proxy GEMM: about kPbWaves waves over the chip (tiles x
+// waves per tile x splits), splits of whole 128-row groups, at most
 // kPbMaxSplits.  Depends on the shape only (the workspace is sized from it).
-constexpr int kPbBlocks = 320;
+constexpr int kPbWaves = 1536;
 constexpr int kPbMaxSplits = 8;
 
 PbSplit proxy_batch_split(int d, int F, int kind) {
     const int tiles = f_pad_of(F, kind) / tile_channels(kind);
+    const int waves = tiles * (kind == 1 ? 4 : 8);
     const int groups = (d + 127) / 128;
-    int ks = (kPbBlocks + tiles - 1) / tiles;
+    int ks = (kPbWaves + waves - 1) / waves;
     if (ks > kPbMaxSplits) ks = kPbMaxSplits;
     if (ks > groups) ks = groups;
     if (ks < 1) ks = 1;
@@ -425,27 +418,34 @@ PbSplit proxy_batch_split(int d, int F, int kind) {
     return r;
 }
 
-template <int KIND, int NG>
+template <int KIND, int NG, int PD>
 static hipError_t go_proxy_batch(const PbArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((k_proxy_batch<KIND, NG>), dim3(a.tiles * a.ks1), dim3(256), 0, s, a);
+    constexpr int NW = KIND == 1 ? 4 : 8;
+    const size_t dyn = (size_t)NW * kPbWave * 2;
+    auto fn = k_proxy_batch<KIND, NG, PD>;
+    if (dyn > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fn, dim3(a.tiles * a.ks1), dim3(NW * 64), dyn, s, a);
     return hipGetLastError();
 }
 
 template <int KIND>
 static hipError_t proxy_batch_ng(const PbArgs& a, hipStream_t s) {
     const int ng = (a.B + 15) / 16;
-    if (ng == 1) return go_proxy_batch<KIND, 1>(a, s);
-    if (ng == 2) return go_proxy_batch<KIND, 2>(a, s);
-    if (ng == 3) return go_proxy_batch<KIND, 3>(a, s);
-    return go_proxy_batch<KIND, 4>(a, s);
+    if (ng == 1) return go_proxy_batch<KIND, 1, 2>(a, s);
+    if (ng == 2) return go_proxy_batch<KIND, 2, 2>(a, s);
+    if (ng == 3) return go_proxy_batch<KIND, 3, 1>(a, s);
+    return go_proxy_batch<KIND, 4, 1>(a, s);
 }
 
 hipError_t launch_proxy_batch(const uint16_t* xm, int B, int d, const ProxyView& p, float* part,
-                              unsigned long long* tcnt, uint32_t gen, float* key, uint32_t* gh,
-                              double* h_tap, float* key_tap, hipStream_t s) {
+                              unsigned long long* tcnt, uint32_t gen, float* key, double* h_tap,
+                              float* key_tap, hipStream_t s) {
     const PbSplit sp = proxy_batch_split(d, p.F, p.kind);
     PbArgs a{xm, p.codes, p.scales, B, d, p.F, p.f_pad, p.groups, p.f_pad / tile_channels(p.kind),
-             sp.ks1, sp.rps, part, tcnt, gen, key, gh, h_tap, key_tap};
+             sp.ks1, sp.rps, part, tcnt, gen, key, h_tap, key_tap};
     return p.kind == 1 ? proxy_batch_ng<1>(a, s) : proxy_batch_ng<2>(a, s);
 }
 
@@ -455,8 +455,8 @@ hipError_t launch_proxy_batch(const uint16_t* xm, int B, int d, const ProxyView&
 // Weight rows and x are K-contiguous, so both operands are 16-byte buffer
 // loads straight into registers; channels that no token keeps, tokens past B
 // and columns past d read at an offset past the end (zeros, no traffic).
-// Four K-steps per stage, two stages in flight; the 4 waves' sums are added
-// in LDS in a fixed order.
+// Two K-steps per stage, kGuDepth stages in flight; the 4 waves' sums are
+// added in LDS in a fixed order.
 // ===========================================================================
 struct GuArgs {
     const uint16_t* x;      // [B][d]
@@ -467,7 +467,8 @@ struct GuArgs {
     int B, d, F, f_pad;
 };
 
-constexpr int kGuSteps = 4;
+constexpr int kGuSteps = 2;
+constexpr int kGuDepth = 4;
 
 template <int NG>
 struct GuStage {
@@ -508,18 +509,19 @@ __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
         xoff[g] = n < a.B ? (uint32_t)n * row_bytes : x_bytes;
     }
     const int kl = 32 * w + 8 * q4;   // this lane's first column within a 128-wide step
+    constexpr int KS = 128 * kGuSteps;   // columns per stage (all 4 waves)
 
-    auto load = [&](int kb, GuStage<NG>& st) {
+    auto load = [&](int s, GuStage<NG>& st) {
 #pragma unroll
-        for (int s = 0; s < kGuSteps; ++s) {
-            const int k = kb + 128 * s + kl;
+        for (int q = 0; q < kGuSteps; ++q) {
+            const int k = KS * s + 128 * q + kl;
             const bool ok = k < d;   // d % 8 == 0: a lane's 8 columns are all in or all out
             const uint32_t kbytes = (uint32_t)k * 2u;
-            st.g[s] = buf_load16(rg, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
-            st.u[s] = buf_load16(ru, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
+            st.g[q] = buf_load16(rg, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
+            st.u[q] = buf_load16(ru, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
 #pragma unroll
             for (int g = 0; g < NG; ++g)
-                st.x[s][g] = buf_load16(rx, ok && xoff[g] < x_bytes ? xoff[g] + kbytes : x_bytes, 0);
+                st.x[q][g] = buf_load16(rx, ok && xoff[g] < x_bytes ? xoff[g] + kbytes : x_bytes, 0);
         }
     };
     f32x4_t ag[NG], au[NG];
@@ -527,26 +529,32 @@ __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
     for (int g = 0; g < NG; ++g) ag[g] = au[g] = zero4();
     auto mma = [&](const GuStage<NG>& st) {
 #pragma unroll
-        for (int s = 0; s < kGuSteps; ++s)
+        for (int q = 0; q < kGuSteps; ++q)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                ag[g] = mfma16(st.g[s], st.x[s][g], ag[g]);
-                au[g] = mfma16(st.u[s], st.x[s][g], au[g]);
+                ag[g] = mfma16(st.g[q], st.x[q][g], ag[g]);
+                au[g] = mfma16(st.u[q], st.x[q][g], au[g]);
             }
     };
 
-    constexpr int KS = 128 * kGuSteps;   // columns per stage (all 4 waves)
-    GuStage<NG> s0, s1;
-    load(0, s0);
-    for (int kb = 0; kb < d; kb += 2 * KS) {
-        load(kb + KS, s1);
-        mma(s0);
-        settle_acc<NG>(ag);
-        settle_acc<NG>(au);
-        load(kb + 2 * KS, s0);
-        mma(s1);
-        settle_acc<NG>(ag);
-        settle_acc<NG>(au);
+    const int nst = (d + KS - 1) / KS;
+    GuStage<NG> ring[kGuDepth];
+#pragma unroll
+    for (int i = 0; i < kGuDepth; ++i) {
+        load(i, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);   // issue order = consumption order
+    }
+    // whole rounds of kGuDepth stages; stages past d read zeros.  The
+    // scheduling barriers keep each refill right behind the products that
+    // free its registers, so kGuDepth - 1 stages stay in flight.
+    for (int s0 = 0; s0 < nst; s0 += kGuDepth) {
+#pragma unroll
+        for (int i = 0; i < kGuDepth; ++i) {
+            mma(ring[i]);
+            __builtin_amdgcn_sched_barrier(0);
+            load(s0 + i + kGuDepth, ring[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g)
@@ -695,7 +703,10 @@ __global__ void __launch_bounds__(256) k_down_batch(DnArgs a) {
     const int nst = (f1 - f0 + 63) / 64;
     DnStage<NG> ring[PD];
 #pragma unroll
-    for (int i = 0; i < PD; ++i) load_stage(i, ring[i]);
+    for (int i = 0; i < PD; ++i) {
+        load_stage(i, ring[i]);
+        __builtin_amdgcn_sched_barrier(0);   // issue order = consumption order
+    }
     for (int s0 = 0; s0 < nst; s0 += PD) {
 #pragma unroll
         for (int i = 0; i < PD; ++i) {

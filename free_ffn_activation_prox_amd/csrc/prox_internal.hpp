@@ -127,8 +127,8 @@ hipError_t launch_select(const float* key, const uint32_t* gh, int B, int d, int
 hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,
                        hipStream_t s);
 hipError_t launch_proxy_batch(const uint16_t* xm, int B, int d, const ProxyView& p, float* part,
-                              unsigned long long* tcnt, uint32_t gen, float* key, uint32_t* gh,
-                              double* h_tap, float* key_tap, hipStream_t s);
+                              unsigned long long* tcnt, uint32_t gen, float* key, double* h_tap,
+                              float* key_tap, hipStream_t s);
 // Gate/up and down over the tokens' masks; *ks_out = partial slices in ypart.
 hipError_t launch_stage2_batch(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
                                const uint16_t* wd, const uint8_t* mask, uint16_t* hb, int B, int d,
