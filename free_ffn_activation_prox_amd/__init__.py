@@ -17,6 +17,11 @@ import os
 from dataclasses import dataclass
 from typing import Dict, Optional, Tuple
 
+# torch first: the library then binds to the HIP runtime torch has loaded, so
+# the process holds one runtime (one device context) whichever module a
+# program imports first.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprox_hip.so")
 
