@@ -17,8 +17,11 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -159,11 +162,18 @@ def main(argv=None):
     gbs = total_b / (ms_per_step * 1e-3) / 1e9
     us_tok = ms_per_step * 1e3 / B
 
-    # dominant kernel: the phase with the largest share of the step
+    # dominant kernel: the phase with the largest share of the step (batch 1:
+    # one kernel per phase; 8+ tokens: stage1 = input selection + proxy GEMM,
+    # stage2 = channel selection + gate/up + down)
     dom = int(np.argmax(phase_ms))
     dom_name = P.PHASES[dom]
     dom_bytes = {0: proxy_b, 1: stage2_b}.get(dom, total_b)
     dom_gbs = dom_bytes / (phase_ms[dom] * 1e-3) / 1e9
+    if B < 8:
+        dom_kernel = {0: "k_stage1", 1: "k_stage2"}.get(dom, "k_reduce_y")
+    else:
+        dom_kernel = {0: "xsel + k_proxy_batch", 1: "k_stage2 (selection) + k_gateup_batch + k_down_batch"}.get(dom, "k_reduce_y")
+    traffic = measured_traffic(wl.name, dom_kernel) if B < 8 else None
 
     out = {
         "metric": METRIC,
@@ -187,10 +197,11 @@ def main(argv=None):
                    "d_model": d, "d_ff": F, "batch": B, "proxy": kind, "k_in": k_in, "k_ff": k_ff,
                    "weight_copies_rotated": copies, "algorithmic_bytes_per_step": int(total_b)},
         "phase_us": {P.PHASES[p]: round(float(phase_ms[p] * 1e3), 2) for p in range(P.N_PHASES)},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "phase": dom_name, "achieved": round(dom_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None, "layer_achieved": round(gbs, 1),
-                     "layer_frac": round(gbs / PEAK_HBM_GBS, 4)},
+                     "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
+                     "layer_achieved": round(gbs, 1), "layer_frac": round(gbs / PEAK_HBM_GBS, 4)},
+        "kernel_sources_sha256": kernel_sources_hash(),
         "setup_s": round(setup_s, 1),
     }
 
@@ -198,6 +209,38 @@ def main(argv=None):
         out["cpu_baseline"] = cpu_baseline(wl, layer, w, xs, k_in, k_ff, total_b / B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def kernel_sources_hash():
+    """sha256 (first 16 hex digits) of the library's kernel sources and header."""
+    files = sorted(glob.glob(os.path.join(ROOT, "free_ffn_activation_prox_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(ROOT, "free_ffn_activation_prox_amd", "csrc", "*.hpp")))
+    files.append(os.path.join(ROOT, "include", "prox.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary of
+    this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy
+    factor), or None when there is none or the kernel sources have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"prox_forward_{workload}_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"Kernel sources sha256: ([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_sources_hash():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 7 and f"prox::{kernel}<" in cells[1]:
+            return int(round((float(cells[5]) + float(cells[6])) * 1e6))
+    return None
 
 
 def copy_calibration(mib, steps):
