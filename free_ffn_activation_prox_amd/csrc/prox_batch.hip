@@ -171,6 +171,10 @@ struct PbArgs {
     float* key_tap;           // [B][F] or null
 };
 
+// Cache policy of a buffer access (gfx950): bit 4 = sc1.  With it a store or
+// load is coherent across the chip's L2 caches, like a device-scope atomic.
+constexpr int kCoherent = 16;
+
 constexpr int kPbRS = 136;    // LDS row stride of a transposed channel, in bf16 (128 + 8)
 constexpr int kPbWave = 2 * 16 * kPbRS;   // bf16 per wave region
 
@@ -331,18 +335,23 @@ __global__ void __launch_bounds__(KIND == 1 ? 256 : 512) k_proxy_batch(PbArgs a)
     // this lane: gate / up of channels ch0 + 4 q4 + i, tokens 16 g + r
     if (a.ks1 > 1) {
         // publish this split's sums; the block that completes the tile adds the
-        // splits in order (device-scope stores and loads, coherent across the
-        // chip's L2 caches; the stores complete before the arrival is counted)
+        // splits in order.  The 16-byte stores and loads carry the sc1 cache
+        // policy (the one the compiler gives device-scope atomics), which keeps
+        // them coherent across the chip's L2 caches; the stores complete before
+        // the arrival is counted.
+        const uint32_t part_bytes = (uint32_t)a.ks1 * 2u * (uint32_t)a.B * (uint32_t)a.f_pad * 4u;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part, part_bytes);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int n = 16 * g + r;
                 if (n < a.B) {
-                    float* dst = a.part + (((size_t)split * 2 + m) * a.B + n) * a.f_pad + ch0 + 4 * q4;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        __hip_atomic_store(dst + i, (float)dacc[m][g][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint32_t off =
+                        ((((uint32_t)split * 2u + m) * (uint32_t)a.B + n) * (uint32_t)a.f_pad + ch0 + 4 * q4) * 4u;
+                    const u32x4_t v = {__float_as_uint((float)dacc[m][g][0]), __float_as_uint((float)dacc[m][g][1]),
+                                       __float_as_uint((float)dacc[m][g][2]), __float_as_uint((float)dacc[m][g][3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rp, (int)off, 0, kCoherent);
                 }
             }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
@@ -368,15 +377,18 @@ __global__ void __launch_bounds__(KIND == 1 ? 256 : 512) k_proxy_batch(PbArgs a)
             for (int g = 0; g < NG; ++g) {
                 const int n = 16 * g + r;
                 if (n < a.B) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        double sum = 0.0;
-                        for (int sp = 0; sp < a.ks1; ++sp)
-                            sum += (double)__hip_atomic_load(
-                                a.part + (((size_t)sp * 2 + m) * a.B + n) * a.f_pad + ch0 + 4 * q4 + i,
-                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        dacc[m][g][i] = sum;
+                    double sum[4] = {0.0, 0.0, 0.0, 0.0};
+                    for (int sp = 0; sp < a.ks1; ++sp) {
+                        const uint32_t off =
+                            ((((uint32_t)sp * 2u + m) * (uint32_t)a.B + n) * (uint32_t)a.f_pad + ch0 + 4 * q4) * 4u;
+                        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rp, (int)off, 0, kCoherent);
+                        sum[0] += (double)__uint_as_float(v.x);
+                        sum[1] += (double)__uint_as_float(v.y);
+                        sum[2] += (double)__uint_as_float(v.z);
+                        sum[3] += (double)__uint_as_float(v.w);
                     }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dacc[m][g][i] = sum[i];
                 }
             }
     }
@@ -450,12 +462,13 @@ hipError_t launch_proxy_batch(const uint16_t* xm, int B, int d, const ProxyView&
 }
 
 // ===========================================================================
-// Gate/up.  Block: 16 channels j0 .. j0 + 15 (the MFMA's M), every token (N,
-// 16 per group), K = d split over the 4 waves in interleaved 32-wide steps.
-// Weight rows and x are K-contiguous, so both operands are 16-byte buffer
-// loads straight into registers; channels that no token keeps, tokens past B
-// and columns past d read at an offset past the end (zeros, no traffic).
-// Two K-steps per stage, kGuDepth stages in flight; the 4 waves' sums are
+// Gate/up.  Block: 16·MTW channels j0 .. (the MFMA's M, MTW tiles of 16 per
+// wave), every token (N, 16 per group), K = d split over the 4 waves, 64
+// columns each per stage.  Weight rows and x are K-contiguous, so both
+// operands are 16-byte buffer loads straight into registers; channels that no
+// token keeps, tokens past B and columns past d read at an offset past the end
+// (zeros, no traffic).  With two M-tiles per wave each x operand feeds four
+// products.  Two K-steps per stage, PD stages in flight; the 4 waves' sums are
 // added in LDS in a fixed order.
 // ===========================================================================
 struct GuArgs {
@@ -468,31 +481,32 @@ struct GuArgs {
 };
 
 constexpr int kGuSteps = 2;
-constexpr int kGuDepth = 4;
 
-template <int NG>
+template <int NG, int MTW>
 struct GuStage {
-    uint4 g[kGuSteps], u[kGuSteps], x[kGuSteps][NG];
+    uint4 g[kGuSteps][MTW], u[kGuSteps][MTW], x[kGuSteps][NG];
 };
 
-template <int NG>
+template <int NG, int MTW>
 __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
-    __shared__ uint32_t used[16];
+    constexpr int PD = MTW == 1 ? 4 : 3;   // stages in flight
+    constexpr int CH = 16 * MTW;           // channels of the block
+    __shared__ uint32_t used[CH];
     __shared__ float red[4][NG][2][4][64];
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int r = l & 15, q4 = l >> 4;
-    const int j0 = blockIdx.x * 16;
+    const int j0 = blockIdx.x * CH;
     const int d = a.d;
 
     // channels of this block that some token keeps
-    if (t < 16) used[t] = 0u;
+    if (t < CH) used[t] = 0u;
     __syncthreads();
-    {
-        const int jr = j0 + (t & 15);
+    for (int c = t % CH, n0 = t / CH; c < CH && n0 < 256 / CH; c += 256) {
+        const int jr = j0 + c;
         uint32_t any = 0;
         if (jr < a.F)
-            for (int n = t >> 4; n < a.B; n += 16) any |= a.mask[(size_t)n * a.F + jr];
-        if (any) used[t & 15] = 1u;
+            for (int n = n0; n < a.B; n += 256 / CH) any |= a.mask[(size_t)n * a.F + jr];
+        if (any) used[c] = 1u;
     }
     __syncthreads();
 
@@ -500,91 +514,109 @@ __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
     const uint32_t w_bytes = (uint32_t)a.F * row_bytes, x_bytes = (uint32_t)a.B * row_bytes;
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.wg_t, w_bytes), ru = make_rsrc(a.wu_t, w_bytes);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, x_bytes);
-    const int j = j0 + r;
-    const uint32_t woff = (j < a.F && used[r]) ? (uint32_t)j * row_bytes : w_bytes;
+    uint32_t woff[MTW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+        const int j = j0 + 16 * mt + r;
+        woff[mt] = (j < a.F && used[16 * mt + r]) ? (uint32_t)j * row_bytes : w_bytes;
+    }
     uint32_t xoff[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         const int n = 16 * g + r;
         xoff[g] = n < a.B ? (uint32_t)n * row_bytes : x_bytes;
     }
-    const int kl = 32 * w + 8 * q4;   // this lane's first column within a 128-wide step
+    // wave w reads columns 64 w .. 64 w + 63 of each stage (whole 128-byte
+    // lines of its rows), lane column 8 q4 in each of the two 32-wide steps
+    const int kl = 64 * w + 8 * q4;
     constexpr int KS = 128 * kGuSteps;   // columns per stage (all 4 waves)
 
-    auto load = [&](int s, GuStage<NG>& st) {
+    auto load = [&](int s, GuStage<NG, MTW>& st) {
 #pragma unroll
         for (int q = 0; q < kGuSteps; ++q) {
-            const int k = KS * s + 128 * q + kl;
+            const int k = KS * s + 32 * q + kl;
             const bool ok = k < d;   // d % 8 == 0: a lane's 8 columns are all in or all out
             const uint32_t kbytes = (uint32_t)k * 2u;
-            st.g[q] = buf_load16(rg, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
-            st.u[q] = buf_load16(ru, ok && woff < w_bytes ? woff + kbytes : w_bytes, 0);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+                st.g[q][mt] = buf_load16(rg, ok && woff[mt] < w_bytes ? woff[mt] + kbytes : w_bytes, 0);
+                st.u[q][mt] = buf_load16(ru, ok && woff[mt] < w_bytes ? woff[mt] + kbytes : w_bytes, 0);
+            }
 #pragma unroll
             for (int g = 0; g < NG; ++g)
                 st.x[q][g] = buf_load16(rx, ok && xoff[g] < x_bytes ? xoff[g] + kbytes : x_bytes, 0);
         }
     };
-    f32x4_t ag[NG], au[NG];
+    f32x4_t ag[MTW][NG], au[MTW][NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) ag[g] = au[g] = zero4();
-    auto mma = [&](const GuStage<NG>& st) {
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ag[mt][g] = au[mt][g] = zero4();
+    auto mma = [&](const GuStage<NG, MTW>& st) {
 #pragma unroll
         for (int q = 0; q < kGuSteps; ++q)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                ag[g] = mfma16(st.g[q], st.x[q][g], ag[g]);
-                au[g] = mfma16(st.u[q], st.x[q][g], au[g]);
-            }
+            for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    ag[mt][g] = mfma16(st.g[q][mt], st.x[q][g], ag[mt][g]);
+                    au[mt][g] = mfma16(st.u[q][mt], st.x[q][g], au[mt][g]);
+                }
     };
 
     const int nst = (d + KS - 1) / KS;
-    GuStage<NG> ring[kGuDepth];
+    GuStage<NG, MTW> ring[PD];
 #pragma unroll
-    for (int i = 0; i < kGuDepth; ++i) {
+    for (int i = 0; i < PD; ++i) {
         load(i, ring[i]);
         __builtin_amdgcn_sched_barrier(0);   // issue order = consumption order
     }
-    // whole rounds of kGuDepth stages; stages past d read zeros.  The
-    // scheduling barriers keep each refill right behind the products that
-    // free its registers, so kGuDepth - 1 stages stay in flight.
-    for (int s0 = 0; s0 < nst; s0 += kGuDepth) {
+    // whole rounds of PD stages; stages past d read zeros.  The scheduling
+    // barriers keep each refill right behind the products that free its
+    // registers, so PD - 1 stages stay in flight.
+    for (int s0 = 0; s0 < nst; s0 += PD) {
 #pragma unroll
-        for (int i = 0; i < kGuDepth; ++i) {
+        for (int i = 0; i < PD; ++i) {
             mma(ring[i]);
             __builtin_amdgcn_sched_barrier(0);
-            load(s0 + i + kGuDepth, ring[i]);
+            load(s0 + i + PD, ring[i]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    // the 4 waves' K quarters, one M-tile at a time: channel j0 + 16 mt + 4 q4 + i, token 16 g + r
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
+    for (int mt = 0; mt < MTW; ++mt) {
+        if (mt > 0) __syncthreads();   // `red` is reused
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            red[w][g][0][i][l] = ag[g][i];
-            red[w][g][1][i][l] = au[g][i];
-        }
-    __syncthreads();
-    // wave w finishes token groups w, w + 4, ...: channel j0 + 4 q4 + i, token 16 g + r
-    for (int g = w; g < NG; g += 4) {
-        const int n = 16 * g + r;
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int jc = j0 + 4 * q4 + i;
-            // channels past F (up to the block's end) get h = 0: the down
-            // projection reads h 8 channels at a time
-            if (n < a.B) {
-                float gg = 0.f, uu = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                red[w][g][0][i][l] = ag[mt][g][i];
+                red[w][g][1][i][l] = au[mt][g][i];
+            }
+        __syncthreads();
+        // wave w finishes token groups w, w + 4, ...
+        for (int g = w; g < NG; g += 4) {
+            const int n = 16 * g + r;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    gg += red[v][g][0][i][l];
-                    uu += red[v][g][1][i][l];
+            for (int i = 0; i < 4; ++i) {
+                const int jc = j0 + 16 * mt + 4 * q4 + i;
+                // channels past F (up to the block's end) get h = 0: the down
+                // projection reads h 8 channels at a time
+                if (n < a.B) {
+                    float gg = 0.f, uu = 0.f;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        gg += red[v][g][0][i][l];
+                        uu += red[v][g][1][i][l];
+                    }
+                    float hv = gg / (1.f + expf(-gg)) * uu;
+                    if (jc >= a.F || !a.mask[(size_t)n * a.F + jc]) hv = 0.f;
+                    const uint32_t hi = bf16_rne(hv);
+                    const uint32_t lo = bf16_rne(hv - __uint_as_float(hi << 16));
+                    a.hb[(size_t)n * a.f_pad + jc] = (uint16_t)hi;
+                    a.hb[((size_t)a.B + n) * a.f_pad + jc] = (uint16_t)lo;
                 }
-                float hv = gg / (1.f + expf(-gg)) * uu;
-                if (jc >= a.F || !a.mask[(size_t)n * a.F + jc]) hv = 0.f;
-                const uint32_t hi = bf16_rne(hv);
-                const uint32_t lo = bf16_rne(hv - __uint_as_float(hi << 16));
-                a.hb[(size_t)n * a.f_pad + jc] = (uint16_t)hi;
-                a.hb[((size_t)a.B + n) * a.f_pad + jc] = (uint16_t)lo;
             }
         }
     }
@@ -617,7 +649,7 @@ struct DnStage {
 
 template <int NG>
 __global__ void __launch_bounds__(256) k_down_batch(DnArgs a) {
-    constexpr int PD = NG <= 2 ? 4 : 2;        // stages in flight
+    constexpr int PD = NG == 1 ? 4 : (NG == 2 ? 3 : 2);   // stages in flight
     constexpr int TILE = kDnCols * kDnRS;      // bf16 per LDS buffer
     __shared__ uint4 lds_raw[2 * TILE / 8];
     uint16_t* lds = reinterpret_cast<uint16_t*>(lds_raw);
@@ -748,7 +780,9 @@ DnSplit down_batch_split(int B, int d, int F) {
 
 template <int NG>
 static hipError_t go_gateup_down(const GuArgs& gu, const DnArgs& dn, hipStream_t s) {
-    hipLaunchKernelGGL(k_gateup_batch<NG>, dim3((gu.F + 15) / 16), dim3(256), 0, s, gu);
+    // two M-tiles per wave when x has two or more token groups (x operand reuse)
+    constexpr int MTW = NG >= 2 ? 2 : 1;
+    hipLaunchKernelGGL((k_gateup_batch<NG, MTW>), dim3((gu.F + 16 * MTW - 1) / (16 * MTW)), dim3(256), 0, s, gu);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_down_batch<NG>, dim3((dn.d + kDnCols - 1) / kDnCols, dn.KS), dim3(256), 0, s, dn);
