@@ -36,6 +36,7 @@ from prox_workloads import gen_weights, gen_x, workloads  # noqa: E402
 METRIC = "sparse FFN-layer µs/token and achieved HBM GB/s (% peak) at 70% sparsity"
 PEAK_HBM_GBS = 8000.0
 LLC_BYTES = 256 << 20
+BATCH_MIN = 4   # the library's switch to the matrix-core path (tokens per call)
 
 
 def algorithmic_bytes(d, F, kind, k_in_rows, k_ch, B):
@@ -162,18 +163,19 @@ def main(argv=None):
     gbs = total_b / (ms_per_step * 1e-3) / 1e9
     us_tok = ms_per_step * 1e3 / B
 
-    # dominant kernel: the phase with the largest share of the step (batch 1:
-    # one kernel per phase; 8+ tokens: stage1 = input selection + proxy GEMM,
-    # stage2 = channel selection + gate/up + down)
+    # dominant kernel: the phase with the largest share of the step (fewer
+    # than BATCH_MIN tokens: one kernel per phase; from BATCH_MIN tokens the
+    # matrix-core path: stage1 = input selection + proxy GEMM, stage2 =
+    # channel selection + gate/up + down)
     dom = int(np.argmax(phase_ms))
     dom_name = P.PHASES[dom]
     dom_bytes = {0: proxy_b, 1: stage2_b}.get(dom, total_b)
     dom_gbs = dom_bytes / (phase_ms[dom] * 1e-3) / 1e9
-    if B < 8:
+    if B < BATCH_MIN:
         dom_kernel = {0: "k_stage1", 1: "k_stage2"}.get(dom, "k_reduce_y")
     else:
         dom_kernel = {0: "xsel + k_proxy_batch", 1: "k_stage2 (selection) + k_gateup_batch + k_down_batch"}.get(dom, "k_reduce_y")
-    traffic = measured_traffic(wl.name, dom_kernel) if B < 8 else None
+    traffic = measured_traffic(wl.name, dom_kernel) if B < BATCH_MIN else None
 
     out = {
         "metric": METRIC,

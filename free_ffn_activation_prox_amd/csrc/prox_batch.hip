@@ -1,10 +1,11 @@
-// Prox sparse SwiGLU FFN for batches of 8 or more tokens (gfx950 matrix cores).
+// Prox sparse SwiGLU FFN for batches of several tokens (gfx950 matrix cores).
 //
 // Each token keeps its own input set and its own channel mask (Prox, Abstract:
 // Stage 1 ranks channels per token, one mask shared by the three projections;
-// tokens are independent problems).  At 8+ tokens nearly every input row and
-// every channel is kept by some token, so both stages become contractions over
-// the union, run on bf16 matrix cores (v_mfma_f32_16x16x32_bf16):
+// tokens are independent problems).  With several tokens most input rows and
+// channels are kept by some token (at 8+ nearly all), so both stages become
+// contractions over the union, run on bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16):
 //
 //   input select  x~_b = x_b on its k_in largest |x| (lower index wins ties),
 //                 0 elsewhere

@@ -1,4 +1,4 @@
-"""GPU parity of the matrix-core path (batches of 8 or more tokens) against
+"""GPU parity of the matrix-core path (batches of 4 or more tokens) against
 the CPU oracle.
 
 Every token of every case is compared with the oracle to the same bar as the
@@ -37,7 +37,7 @@ def _report(label, st):
 
 
 @pytest.mark.parametrize("kind", ["int8", "int4"])
-@pytest.mark.parametrize("d,F,B", [(1024, 1000, 8), (512, 2000, 17), (640, 333, 33), (256, 700, 64)])
+@pytest.mark.parametrize("d,F,B", [(1024, 1000, 8), (512, 2000, 17), (640, 333, 33), (256, 700, 64), (768, 900, 4)])
 def test_batch_shapes(kind, d, F, B):
     print(f"[batch] case {kind} d={d} F={F} B={B}", flush=True)
     c = _case(d, F, B, seed=d + F + B, kind=kind)
