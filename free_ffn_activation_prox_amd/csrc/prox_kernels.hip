@@ -397,40 +397,80 @@ __device__ __forceinline__ void consume_chunk_i8(const Chunk& c, double (&ag)[8]
 
 // int4 chunk: 16 gate + 16 up channels of the lane; the inner sums of a
 // 128-input group are scaled into og/ou when the row's group changes.
-__device__ __forceinline__ void consume_chunk_i4(const Chunk& c, const float* sgp, const float* sup,
-                                                 int f_pad, int& cur, double (&ag)[16], double (&au)[16],
-                                                 double (&og)[16], double (&ou)[16]) {
+// int4: g~ = sum over groups of s_group * (sum over the group's rows of x q).
+// A chunk whose x exponents span at most 5 binades sums its 8 products per
+// channel exactly in fp32 (x has 8 significant bits, |q| <= 8, 8 terms: every
+// partial sum is an integer below 2^21 in units of the smallest product's
+// last bit); the sum is scaled in fp64 into the lane's totals.  Other chunks
+// add x q s row by row in fp64 (x q is exact).  `sg`, `su` hold the current
+// group's scales of the lane's 16 channels; they are reloaded when the group
+// changes, which is rare because a slot takes consecutive kept rows.
+struct I4State {
+    int cur;
+    float sg[16], su[16];
+};
+
+__device__ __forceinline__ void i4_set_group(I4State& st, int g, const float* sgp, const float* sup, int f_pad) {
+    const float4* s4g = reinterpret_cast<const float4*>(sgp + (size_t)g * f_pad);
+    const float4* s4u = reinterpret_cast<const float4*>(sup + (size_t)g * f_pad);
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-        const int g = (int)(c.e[u] >> 16) >> 7;
-        if (g != cur) {
-            if (cur >= 0) {
-                const float4* s4g = reinterpret_cast<const float4*>(sgp + (size_t)cur * f_pad);
-                const float4* s4u = reinterpret_cast<const float4*>(sup + (size_t)cur * f_pad);
+    for (int q = 0; q < 4; ++q) {
+        const float4 fg = s4g[q], fu = s4u[q];
+        st.sg[4 * q] = fg.x; st.sg[4 * q + 1] = fg.y; st.sg[4 * q + 2] = fg.z; st.sg[4 * q + 3] = fg.w;
+        st.su[4 * q] = fu.x; st.su[4 * q + 1] = fu.y; st.su[4 * q + 2] = fu.z; st.su[4 * q + 3] = fu.w;
+    }
+    st.cur = g;
+}
+
+__device__ __forceinline__ void i4_flush(const I4State& st, float (&pg)[16], float (&pu)[16], double (&og)[16],
+                                         double (&ou)[16]) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 fg = s4g[q], fu = s4u[q];
-                    og[4 * q + 0] = fma(ag[4 * q + 0], (double)fg.x, og[4 * q + 0]);
-                    og[4 * q + 1] = fma(ag[4 * q + 1], (double)fg.y, og[4 * q + 1]);
-                    og[4 * q + 2] = fma(ag[4 * q + 2], (double)fg.z, og[4 * q + 2]);
-                    og[4 * q + 3] = fma(ag[4 * q + 3], (double)fg.w, og[4 * q + 3]);
-                    ou[4 * q + 0] = fma(au[4 * q + 0], (double)fu.x, ou[4 * q + 0]);
-                    ou[4 * q + 1] = fma(au[4 * q + 1], (double)fu.y, ou[4 * q + 1]);
-                    ou[4 * q + 2] = fma(au[4 * q + 2], (double)fu.z, ou[4 * q + 2]);
-                    ou[4 * q + 3] = fma(au[4 * q + 3], (double)fu.w, ou[4 * q + 3]);
-                }
+    for (int q = 0; q < 16; ++q) {
+        og[q] = fma((double)pg[q], (double)st.sg[q], og[q]);
+        ou[q] = fma((double)pu[q], (double)st.su[q], ou[q]);
+        pg[q] = pu[q] = 0.f;
+    }
+}
+
+__device__ __forceinline__ void consume_chunk_i4(const Chunk& c, const float* sgp, const float* sup, int f_pad,
+                                                 I4State& st, double (&og)[16], double (&ou)[16]) {
+    if (chunk_exact32(c)) {
+        float pg[16], pu[16];
 #pragma unroll
-                for (int q = 0; q < 16; ++q) ag[q] = au[q] = 0.0;
+        for (int q = 0; q < 16; ++q) pg[q] = pu[q] = 0.f;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            // an empty entry (past the run: x = 0, reads zeros) keeps the group
+            const int g = c.e[u] ? (int)(c.e[u] >> 16) >> 7 : st.cur;
+            if (g != st.cur) {
+                if (st.cur >= 0) i4_flush(st, pg, pu, og, ou);
+                i4_set_group(st, g, sgp, sup, f_pad);
             }
-            cur = g;
-        }
-        const double xd = (double)bf16f(c.e[u] & 0xffffu);
+            const float xf = bf16f(c.e[u] & 0xffffu);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            ag[q] = fma(xd, (double)sext4(c.v[u].x, q), ag[q]);
-            ag[q + 8] = fma(xd, (double)sext4(c.v[u].y, q), ag[q + 8]);
-            au[q] = fma(xd, (double)sext4(c.v[u].z, q), au[q]);
-            au[q + 8] = fma(xd, (double)sext4(c.v[u].w, q), au[q + 8]);
+            for (int q = 0; q < 8; ++q) {
+                pg[q] = fmaf(xf, (float)sext4(c.v[u].x, q), pg[q]);
+                pg[q + 8] = fmaf(xf, (float)sext4(c.v[u].y, q), pg[q + 8]);
+                pu[q] = fmaf(xf, (float)sext4(c.v[u].z, q), pu[q]);
+                pu[q + 8] = fmaf(xf, (float)sext4(c.v[u].w, q), pu[q + 8]);
+            }
+        }
+        if (st.cur >= 0) i4_flush(st, pg, pu, og, ou);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const int g = c.e[u] ? (int)(c.e[u] >> 16) >> 7 : st.cur;
+            if (g != st.cur) i4_set_group(st, g, sgp, sup, f_pad);
+            if (st.cur < 0) continue;   // nothing kept yet: every entry is empty
+            const float xf = bf16f(c.e[u] & 0xffffu);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                // x q is exact in fp32 (8 + 4 significant bits)
+                og[q] = fma((double)(xf * (float)sext4(c.v[u].x, q)), (double)st.sg[q], og[q]);
+                og[q + 8] = fma((double)(xf * (float)sext4(c.v[u].y, q)), (double)st.sg[q + 8], og[q + 8]);
+                ou[q] = fma((double)(xf * (float)sext4(c.v[u].z, q)), (double)st.su[q], ou[q]);
+                ou[q + 8] = fma((double)(xf * (float)sext4(c.v[u].w, q)), (double)st.su[q + 8], ou[q + 8]);
+            }
         }
     }
 }
@@ -501,24 +541,24 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
             double og[NV], ou[NV];
 #pragma unroll
             for (int c = 0; c < NV; ++c) og[c] = ou[c] = 0.0;
-            int cur = -1;
-            load_chunk(list, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
-            for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
-                load_chunk(list, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
-                consume_chunk_i4(c0, sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
-                settle_d(og);
-                load_chunk(list, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
-                consume_chunk_i4(c1, sgp, sup, a.p.f_pad, cur, ag, au, og, ou);
-                settle_d(og);
-            }
-            if (cur >= 0) {
-                const float* sg = sgp + (size_t)cur * a.p.f_pad;
-                const float* su = sup + (size_t)cur * a.p.f_pad;
+            I4State st;
+            st.cur = -1;
 #pragma unroll
-                for (int c = 0; c < NV; ++c) {
-                    og[c] = fma(ag[c], (double)sg[c], og[c]);
-                    ou[c] = fma(au[c], (double)su[c], ou[c]);
-                }
+            for (int q = 0; q < 16; ++q) st.sg[q] = st.su[q] = 0.f;
+            // each slot takes a contiguous run of chunks: consecutive kept rows
+            // share their 128-row group, so the group scales are applied (and
+            // loaded) once per group change instead of once per chunk
+            const int n = ce - ca;
+            const int cs0 = ca + (int)((long long)slot * n / kSlots);
+            const int cs1 = ca + (int)((long long)(slot + 1) * n / kSlots);
+            load_chunk(list, k_in, cs0, cs1, crs, codes_bytes, tile_off, lane_off, c0);
+            for (int ch = cs0; ch < cs1; ch += 2) {
+                load_chunk(list, k_in, ch + 1, cs1, crs, codes_bytes, tile_off, lane_off, c1);
+                consume_chunk_i4(c0, sgp, sup, a.p.f_pad, st, og, ou);
+                settle_d(og);
+                load_chunk(list, k_in, ch + 2, cs1, crs, codes_bytes, tile_off, lane_off, c0);
+                consume_chunk_i4(c1, sgp, sup, a.p.f_pad, st, og, ou);
+                settle_d(og);
             }
 #pragma unroll
             for (int c = 0; c < NV; ++c) {
