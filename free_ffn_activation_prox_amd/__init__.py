@@ -185,8 +185,9 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
                 idx=None, workspace=None, taps: bool = False, events=None, stream=None):
     """Sparse SwiGLU forward for x [B][d] bf16.  Returns (y fp32 [B][d], mask u8 [B][F],
     idx int32 [B][k_ff]) and, with ``taps``, a dict of in_idx / key / h_hat.
-    ``events``: N_PHASES + 1 torch.cuda.Event(enable_timing=True) recorded at the
-    phase boundaries on the launch stream (measurement hook)."""
+    ``events``: N_PHASES + 1 events recorded at the phase boundaries on the
+    launch stream (measurement hook): torch.cuda.Event(enable_timing=True)
+    objects already recorded once, or raw hipEvent_t handles (int)."""
     import torch
     if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
         raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
@@ -203,7 +204,7 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
         workspace = alloc_workspace(d, F, B, proxy.kind, dev)
     sp = _stream_ptr(stream)
     if events is not None:
-        arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        arr = (ctypes.c_void_p * len(events))(*[getattr(e, "cuda_event", e) for e in events])
         ct = _Taps(None, None, None, arr, len(events), 0)
         _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
                                           ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),

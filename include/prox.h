@@ -116,7 +116,11 @@ typedef struct {
  *   h_hat  [batch][d_ff]   fp64 approximate intermediate h~_j (signed)
  * Measurement hook (host, nullable): `events` holds n_events >= PROX_N_PHASES + 1
  * hipEvent_t handles (as void*) created by the caller; events[0] is recorded on
- * the stream before the first launch and events[p + 1] after kernel p.       */
+ * the stream before the first launch and events[p + 1] after phase p.  A phase
+ * is one kernel below 4 tokens per call; from 4 tokens stage 1 is the input
+ * selection and the proxy GEMM, stage 2 the channel selection, gate/up and
+ * down projections.  Events created with hipEventDisableSystemFence keep the
+ * marks from writing back and invalidating caches between the kernels.      */
 typedef struct {
     int32_t* in_idx;
     float* key;

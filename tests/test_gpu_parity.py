@@ -174,3 +174,23 @@ def test_many_equal_keys(F, n_patterns):
         for b in range(c.B):
             omask = O.stage1_token(c.x[b], pg, pu, k_in, k_ff)[5]
             assert np.array_equal(np.flatnonzero(mask[b].cpu().numpy()), np.asarray(omask)), (F, sp, b)
+
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_measurement_events(B):
+    # the measurement hook leaves the outputs unchanged and gives positive
+    # phase times
+    import free_ffn_activation_prox_amd as P
+    c = _case(1024, 1500, B, seed=12, kind="int8")
+    ref = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 450)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(P.N_PHASES + 1)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    out = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 450, events=ev)
+    torch.cuda.synchronize()
+    for u, v in zip(out, ref):
+        assert torch.equal(u, v)
+    times = [ev[p].elapsed_time(ev[p + 1]) for p in range(P.N_PHASES)]
+    assert all(0.0 < t < 1000.0 for t in times), times
