@@ -119,8 +119,7 @@ typedef struct {
  * the stream before the first launch and events[p + 1] after phase p.  A phase
  * is one kernel below 4 tokens per call; from 4 tokens stage 1 is the input
  * selection and the proxy GEMM, stage 2 the channel selection, gate/up and
- * down projections.  Events created with hipEventDisableSystemFence keep the
- * marks from writing back and invalidating caches between the kernels.      */
+ * down projections.                                                          */
 typedef struct {
     int32_t* in_idx;
     float* key;
