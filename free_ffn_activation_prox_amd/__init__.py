@@ -23,7 +23,8 @@ from typing import Dict, Optional, Tuple
 import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libprox_hip.so")
+# PROX_HIP_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PROX_HIP_LIB") or os.path.join(_HERE, "libprox_hip.so")
 
 PROX_OK = 0
 KINDS = {"int8": 1, "int4": 2}

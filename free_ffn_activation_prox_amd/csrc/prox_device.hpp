@@ -276,18 +276,25 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int krem,
 // above.  Returns false when the bins do not add up to n, i.e. the histogram
 // is not the one of these keys; the caller then ranks without it.
 // Requires 1 <= k <= n.
+// This thread's bins of a histogram in global memory, as block_hist_bin_regs
+// takes them: c[i] = bin NB - (t + 1) * PER + i (16-byte loads).
 template <int NT, int NB>
-__device__ bool block_hist_bin(const uint32_t* __restrict__ gh, int k, int n, int shift, int* sc,
-                               SelectState& st) {
-    constexpr int PER = NB / NT;   // bins per thread, descending from the top
+__device__ __forceinline__ void load_hist_bins(const uint32_t* __restrict__ gh, uint32_t (&c)[NB / NT]) {
+    constexpr int PER = NB / NT;
     static_assert(PER % 4 == 0 && PER * NT == NB, "16-byte loads of whole bins");
     const uint4* src = reinterpret_cast<const uint4*>(gh + NB - ((int)threadIdx.x + 1) * PER);
-    uint32_t c[PER];   // c[i] = bin NB - (t + 1) * PER + i
 #pragma unroll
     for (int v = 0; v < PER / 4; ++v) {
         const uint4 u = src[v];
         c[4 * v] = u.x; c[4 * v + 1] = u.y; c[4 * v + 2] = u.z; c[4 * v + 3] = u.w;
     }
+}
+
+// block_hist_bin with this thread's bins already in registers (load_hist_bins).
+template <int NT, int NB>
+__device__ __forceinline__ bool block_hist_bin_regs(const uint32_t (&c)[NB / NT], int k, int n, int shift, int* sc,
+                                                    SelectState& st) {
+    constexpr int PER = NB / NT;
     // A stale histogram may hold anything.  Bins are checked one by one, so a
     // thread's contribution is its true sum (no wrap) or n + 1; the block
     // total is n exactly when no bin is out of range and the bins add up.
@@ -316,11 +323,19 @@ __device__ bool block_hist_bin(const uint32_t* __restrict__ gh, int k, int n, in
     return true;
 }
 
+template <int NT, int NB>
+__device__ __forceinline__ bool block_hist_bin(const uint32_t* __restrict__ gh, int k, int n, int shift, int* sc,
+                                               SelectState& st) {
+    uint32_t c[NB / NT];
+    load_hist_bins<NT, NB>(gh, c);
+    return block_hist_bin_regs<NT, NB>(c, k, n, shift, sc, st);
+}
+
 // The coarse digit from the block's own keys: one radix digit of <= 11 bits
 // in a window that starts at the highest bit set in any key (keys < 2^nbits).
 // Same outputs as block_hist_bin.  Requires 1 <= k <= number of valid keys.
 template <int P, int NT>
-__device__ SelectState block_coarse_bin(const uint32_t (&key)[P], const bool (&valid)[P], int k,
+__device__ __forceinline__ SelectState block_coarse_bin(const uint32_t (&key)[P], const bool (&valid)[P], int k,
                                         int nbits, uint32_t* hist, int* sc) {
     int kmax = 0;
 #pragma unroll
@@ -349,7 +364,7 @@ __device__ SelectState block_coarse_bin(const uint32_t (&key)[P], const bool (&v
 // Remaining digits over the candidate array.  T = the k-th largest key,
 // cgt = number of keys > T.
 template <int NT>
-__device__ void block_select_refine(SelectState& st, const uint32_t* cand, uint32_t& T, int& cgt,
+__device__ __forceinline__ void block_select_refine(SelectState& st, const uint32_t* cand, uint32_t& T, int& cgt,
                                     uint32_t* hist, int* sc) {
     while (st.shift > 0) {
         const int dw = st.shift >= 11 ? 11 : st.shift;

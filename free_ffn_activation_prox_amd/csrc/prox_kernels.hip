@@ -255,7 +255,7 @@ __device__ __forceinline__ bool chunk_exact32(const Chunk& c) {
 // of (keys > T, keys == T) places every kept input, the first k_in - #(> T)
 // keys equal to T in index order.  LDS: hist >= 2048 + 16 + 64 words.
 template <int PX>
-__device__ void stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32_t* hist, int* sc) {
+__device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32_t* hist, int* sc) {
     constexpr int NT = kS1Threads;
     const int t = threadIdx.x, lane = t & 63;
     const int d = a.d, k_in = a.k_in;
@@ -841,20 +841,26 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
     }
+    // keys and the key histogram's bins, requested together
     uint32_t kb[PK];
+    uint32_t cbin[kGhBins / NT];
     {
         bool valid[PK];
         load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
+        load_hist_bins<NT, kGhBins>(a.gh + (size_t)b * kGhBins, cbin);
         // keys past F: negative as int, below every bin of a valid key
 #pragma unroll
         for (int q = 0; q < PK; ++q) kb[q] = valid[q] ? kb[q] : 0x80000000u;
     }
-    // every key in LDS too (index order), for the candidates' values
-    if (t * PK < F) {
+    // every key in LDS too (index order), for the slow paths (written after
+    // the candidate count is known)
+    auto keys_to_lds = [&]() {
+        if (t * PK < F) {
 #pragma unroll
-        for (int q = 0; q < PK; q += 4)
-            if (t * PK + q < F) *reinterpret_cast<uint4*>(keys + t * PK + q) = make_uint4(kb[q], kb[q + 1], kb[q + 2], kb[q + 3]);
-    }
+            for (int q = 0; q < PK; q += 4)
+                if (t * PK + q < F) *reinterpret_cast<uint4*>(keys + t * PK + q) = make_uint4(kb[q], kb[q + 1], kb[q + 2], kb[q + 3]);
+        }
+    };
     // the first NT channels of the range, one per thread
     const uint32_t own0 = t < L ? __float_as_uint(keyb[r0 + t]) : 0u;
     if (STREAM && t == 0) chan[0] = 0;                     // row 0 stands in for an empty list
@@ -863,7 +869,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const bool all = k >= F, none = k == 0;
     SelectState st{0u, 0, 0, 0, 0};
     if (!all && !none) {
-        if (!block_hist_bin<NT, kGhBins>(a.gh + (size_t)b * kGhBins, k, F, kGhShift, sc, st)) {
+        if (!block_hist_bin_regs<NT, kGhBins>(cbin, k, F, kGhShift, sc, st)) {
             bool valid[PK];
 #pragma unroll
             for (int q = 0; q < PK; ++q) valid[q] = (int)kb[q] >= 0;
@@ -894,6 +900,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int C = (int)((uint32_t)tot >> 16);            // certain keys in all
     const int crank0 = (int)(pre >> 16), cp0 = (int)(pre & 0xffffu);
     const bool listed = ncand <= kCandCap;                // candidates compacted (else the slow path)
+    if (!listed || ncand > kSmallCand) keys_to_lds();     // the slow paths read every key from LDS
     // this block's share of the certain keys: ranks [c0, c1)
     const int c0 = (int)((long long)w * C / W2), c1 = (int)((long long)(w + 1) * C / W2);
     int nc = listed ? c1 - c0 : 0;
@@ -910,13 +917,13 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
                 ++cr;
             }
         }
-        uint64_t m = cdm;
         int cp = cp0;
-        while (m) {
-            const int q = __builtin_ctzll(m);
-            m &= m - 1;
-            cidx[cp] = (uint16_t)(t * PK + q);
-            cval[cp++] = keys[t * PK + q];                 // written by this thread above
+#pragma unroll
+        for (int q = 0; q < PK; ++q) {
+            if ((cdm >> q) & 1ull) {
+                cidx[cp] = (uint16_t)(t * PK + q);
+                cval[cp++] = kb[q];
+            }
         }
     }
     if (t == r0 / PK) {                                    // counts before the range
@@ -939,27 +946,25 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         if (ncand > 0) {
             const int need = st.krem;                     // candidates to keep
             if (ncand <= kSmallCand) {
-                bool kept = false;
-                if (t < ncand) {
-                    // rank = candidates before this one in (key descending,
-                    // index ascending), 8 per step (cidx has 64 spare entries;
-                    // entries past ncand are masked)
-                    const uint32_t v = cval[t];
-                    int rank = 0;
-                    for (int i = 0; i < ncand; i += 8) {
-                        const uint4 a4 = *reinterpret_cast<const uint4*>(cval + i);
-                        const uint4 b4 = *reinterpret_cast<const uint4*>(cval + i + 4);
-                        const uint32_t u[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                        for (int kk = 0; kk < 8; ++kk) {
-                            const int ii = i + kk;
-                            rank += (ii < ncand && (u[kk] > v || (u[kk] == v && ii < t))) ? 1 : 0;
-                        }
+                // rank of candidate c = candidates before it in (key
+                // descending, index ascending); S = NT / ncand (a power of
+                // two, <= 64) consecutive lanes share candidate c, each
+                // comparing every S-th candidate, then add their counts
+                int S = 64;
+                while (S * ncand > NT) S >>= 1;
+                const int c = t / S, p = t & (S - 1);
+                int rank = 0;
+                const uint32_t v = c < ncand ? cval[c] : 0u;
+                if (c < ncand) {
+                    for (int i = p; i < ncand; i += S) {
+                        const uint32_t u = cval[i];
+                        rank += (u > v || (u == v && i < c)) ? 1 : 0;
                     }
-                    kept = rank < need;
                 }
+                for (int m = S >> 1; m >= 1; m >>= 1) rank += __shfl_xor(rank, m, 64);
+                const bool kept = c < ncand && p == 0 && rank < need;
                 lds_barrier();
-                if (kept) cidx[t] |= 0x8000u;
+                if (kept) cidx[c] |= 0x8000u;
             } else {
                 // many candidates: remaining bits by histogram over the keys
                 // of the threshold bin, then ties in index order
@@ -1042,7 +1047,9 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     }
     const int kept_before = cert_before + kc_before;
 
-    // ---- the range: kept flags, idx and mask
+    // ---- the range: kept flags, idx and mask (after the stream: nothing in
+    // the stream depends on them)
+    auto write_range = [&]() {
     if (listed && (a.idx || a.mask)) {
         int nk = 0, nd_run = 0;
         for (int c0r = 0; c0r < L; c0r += NT) {
@@ -1062,9 +1069,13 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             nk += t2[0];
         }
     }
+    };
     const int n = nc + nks;
     lds_barrier();
-    if constexpr (!STREAM) return;   // selection only: mask and idx are written
+    if constexpr (!STREAM) {         // selection only: mask and idx are written
+        write_range();
+        return;
+    }
 
     // ---- sparse SwiGLU: group 0 = entries [0, E), then [E, n) G at a time.
     // The loads are unconditional and the loop has no exit from its middle:
@@ -1086,6 +1097,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         settle(yacc);
     }
     if (gi < groups) consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
+    write_range();
     float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
