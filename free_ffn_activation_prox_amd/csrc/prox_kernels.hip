@@ -1143,8 +1143,10 @@ hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t
                          int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask,
                          float* ypart, hipStream_t s) {
     Stage2Args a{x, wg_t, wu_t, wd, key, gh, d, F, f_pad, k_ff, W2, idx, mask, ypart};
-    if (d <= 4096) return stage2_pk<1, 4, true>(a, B, s);
-    if (d <= 8192) return stage2_pk<2, 2, true>(a, B, s);
+    // channels per group: the fewest that keep the stream at its rate (more
+    // rows in flight per block measured slower on the 4096 and 8192 shapes)
+    if (d <= 4096) return stage2_pk<1, 2, true>(a, B, s);
+    if (d <= 8192) return stage2_pk<2, 1, true>(a, B, s);
     return stage2_pk<4, 1, true>(a, B, s);
 }
 
