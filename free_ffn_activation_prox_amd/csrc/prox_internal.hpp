@@ -60,8 +60,11 @@ inline S1Geom s1_geom(int k_in, int F, int kind, int batch, int n_cu) {
     // int8 tiles are cheap enough per row to be bound by the stream: with no
     // more tiles than blocks each block takes one whole tile (no partial sums
     // to combine).  int4 rows cost more arithmetic per byte: its items are
-    // always spread over every block.
+    // spread over the blocks, in whole fractions of a tile when the tiles are
+    // fewer than the blocks (no block then spans two tiles, so a block combines
+    // split sums only at its end, never in the middle of its stream).
     if (kind == 1 && g.tiles < nb) nb = g.tiles;
+    else if (g.tiles <= nb) nb = g.tiles * (nb / g.tiles);
     const long long T = (long long)g.tiles * g.nch;
     if (nb > T) nb = (int)T;
     g.nb1 = nb;
