@@ -270,6 +270,29 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int krem,
     lds_barrier();
 }
 
+// find_bin for nb = 4 * NT bins: thread t owns bins nb-1-4t .. nb-4-4t (one
+// 16-byte LDS read; `hist` 16-byte aligned).
+template <int NT>
+__device__ __forceinline__ void find_bin4(const uint32_t* hist, int krem, int* sc, uint32_t& digit, int& above) {
+    constexpr int nb = 4 * NT;
+    const int t = threadIdx.x;
+    const uint4 u = *reinterpret_cast<const uint4*>(hist + nb - 4 - 4 * t);
+    const int c0 = (int)u.w, c1 = (int)u.z, c2 = (int)u.y, c3 = (int)u.x;   // descending bins
+    int tot;
+    const int cum = block_excl_scan<NT>(c0 + c1 + c2 + c3, sc, tot);
+    if (cum < krem && krem <= cum + c0 + c1 + c2 + c3) {
+        const int top = nb - 1 - 4 * t;
+        if (krem <= cum + c0) { sc[20] = top; sc[21] = cum; }
+        else if (krem <= cum + c0 + c1) { sc[20] = top - 1; sc[21] = cum + c0; }
+        else if (krem <= cum + c0 + c1 + c2) { sc[20] = top - 2; sc[21] = cum + c0 + c1; }
+        else { sc[20] = top - 3; sc[21] = cum + c0 + c1 + c2; }
+    }
+    lds_barrier();
+    digit = (uint32_t)sc[20];
+    above = sc[21];
+    lds_barrier();
+}
+
 // The coarse digit from a histogram built outside the block: NB bins of
 // key >> shift over the n valid keys, in global memory.  On success st holds
 // the threshold bin (prefix), `above` = keys in higher bins and krem = k -

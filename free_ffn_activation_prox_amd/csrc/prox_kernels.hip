@@ -277,20 +277,31 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         for (int q = 0; q < PX; ++q) atomicAdd(&hist[key[q] >= 0 ? (key[q] >> 4) : 2048 + 16], 1u);
         lds_barrier();
         uint32_t tb;
-        find_bin<NT>(hist, 2048, k_in, sc, tb, cgt);
+        static_assert(NT * 4 == 2048, "one 16-byte read of 4 bins per thread");
+        find_bin4<NT>(hist, k_in, sc, tb, cgt);
 #pragma unroll
         for (int q = 0; q < PX; ++q)
             if (key[q] >= 0 && (key[q] >> 4) == (int)tb) atomicAdd(&hist2[key[q] & 15], 1u);
         lds_barrier();
+        // every thread: the 16 low-bit bins in four 16-byte reads, then the
+        // same answer from registers
+        uint32_t h16[16];
+#pragma unroll
+        for (int v = 0; v < 16; v += 4) {
+            const uint4 u = *reinterpret_cast<const uint4*>(hist2 + v);
+            h16[v] = u.x; h16[v + 1] = u.y; h16[v + 2] = u.z; h16[v + 3] = u.w;
+        }
         int cum = cgt;
         T = (int)(tb << 4);
-        for (int v = 15; v >= 0; --v) {                    // every thread: same answer
-            const int c = (int)hist2[v];
-            if (cum + c >= k_in) {
+        bool found = false;
+#pragma unroll
+        for (int v = 15; v >= 0; --v) {
+            const int c = (int)h16[v];
+            if (!found && cum + c >= k_in) {
                 T = (int)(tb << 4) + v;
-                break;
+                found = true;
             }
-            cum += c;
+            cum += found ? 0 : c;
         }
         cgt = cum;                                         // keys > T
     }
@@ -487,7 +498,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     constexpr int NV = KIND == 1 ? 8 : 16;               // channels per lane
     constexpr int NW = kS1Threads / kWave;
     extern __shared__ uint32_t dyn[];
-    __shared__ uint32_t hist[2048 + 16 + 64];
+    __shared__ __align__(16) uint32_t hist[2048 + 16 + 64];
     __shared__ int sc[24];
     __shared__ double red[8][2][TC];
     __shared__ double gsum[2][TC];
