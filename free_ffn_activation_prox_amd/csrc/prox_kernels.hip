@@ -164,6 +164,9 @@ struct Stage1Args {
 };
 
 constexpr int kS1Threads = 512;
+// byte flags of the chunks after the kept-input list (k_in + 64 words) in the
+// dynamic LDS: word offset
+__host__ __device__ __forceinline__ int s1_flags_off(int k_in) { return (k_in + 64 + 3) & ~3; }
 constexpr int kSlots = 64;
 constexpr int kChunk = 8;
 
@@ -216,18 +219,25 @@ __device__ __forceinline__ void stage1_score(const Stage1Args& a, int b, int j, 
 struct Chunk {
     uint32_t e[kChunk];
     uint4 v[kChunk];
+    bool exact;          // x of the chunk span at most 5 binades, none subnormal
 };
 
-__device__ __forceinline__ void load_chunk(const uint32_t* list, int k_in, int ch, int ch_end,
-                                           __amdgpu_buffer_rsrc_t codes, uint32_t codes_bytes,
+__device__ __forceinline__ void load_chunk(const uint32_t* list, const uint8_t* exact, int k_in, int ch,
+                                           int ch_end, __amdgpu_buffer_rsrc_t codes, uint32_t codes_bytes,
                                            uint32_t tile_off, uint32_t lane_off, Chunk& c) {
     const int r0 = ch * kChunk;
     const int n = ch < ch_end ? min(kChunk, k_in - r0) : 0;
+    // the 8 entries in two 16-byte LDS reads (a chunk past the list reads
+    // entries 0..7, all masked; the list has 64 spare words past k_in)
+    const int rr = n > 0 ? r0 : 0;
+    const uint4 ea = *reinterpret_cast<const uint4*>(list + rr);
+    const uint4 eb = *reinterpret_cast<const uint4*>(list + rr + 4);
+    const uint32_t ev[kChunk] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
+    c.exact = n > 0 ? exact[ch] != 0 : true;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
-        const uint32_t e = list[u < n ? r0 + u : 0];
-        c.e[u] = u < n ? e : 0u;
-        const uint32_t off = u < n ? (e >> 16) * (uint32_t)kTileRowBytes + lane_off : codes_bytes;
+        c.e[u] = u < n ? ev[u] : 0u;
+        const uint32_t off = u < n ? (ev[u] >> 16) * (uint32_t)kTileRowBytes + lane_off : codes_bytes;
         c.v[u] = buf_load16(codes, off, tile_off);
     }
 }
@@ -355,6 +365,16 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         }
     }
     lds_barrier();
+    // each chunk's exactness flag (entries past k_in are empty)
+    uint8_t* exact = reinterpret_cast<uint8_t*>(list + s1_flags_off(k_in));
+    const int nch = (k_in + kChunk - 1) / kChunk;
+    for (int ch = t; ch < nch; ch += NT) {
+        Chunk c;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) c.e[u] = ch * kChunk + u < k_in ? list[ch * kChunk + u] : 0u;
+        exact[ch] = chunk_exact32(c) ? 1 : 0;
+    }
+    lds_barrier();
 }
 
 // Unsigned byte c of w as float (one conversion instruction).
@@ -367,7 +387,7 @@ __device__ __forceinline__ float ubyte_f(uint32_t w, int c) { return (float)((w 
 // product below 2^21 and every partial sum below 2^24: all steps are exact,
 // and so is the final difference (its value is the exact sum x*q).
 __device__ __forceinline__ void consume_chunk_i8(const Chunk& c, double (&ag)[8], double (&au)[8]) {
-    if (chunk_exact32(c)) {
+    if (c.exact) {
         float sg[8], su[8], sx = 0.f;
 #pragma unroll
         for (int q = 0; q < 8; ++q) sg[q] = su[q] = 0.f;
@@ -445,7 +465,7 @@ __device__ __forceinline__ void i4_flush(const I4State& st, float (&pg)[16], flo
 
 __device__ __forceinline__ void consume_chunk_i4(const Chunk& c, const float* sgp, const float* sup, int f_pad,
                                                  I4State& st, double (&og)[16], double (&ou)[16]) {
-    if (chunk_exact32(c)) {
+    if (c.exact) {
         float pg[16], pu[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) pg[q] = pu[q] = 0.f;
@@ -497,7 +517,8 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     constexpr int TC = KIND == 1 ? 64 : 128;            // channels per tile
     constexpr int NV = KIND == 1 ? 8 : 16;               // channels per lane
     constexpr int NW = kS1Threads / kWave;
-    extern __shared__ uint32_t dyn[];
+    extern __shared__ uint4 dyn_v[];               // 16-byte aligned (16-byte list reads)
+    uint32_t* dyn = reinterpret_cast<uint32_t*>(dyn_v);
     __shared__ __align__(16) uint32_t hist[2048 + 16 + 64];
     __shared__ int sc[24];
     __shared__ double red[8][2][TC];
@@ -506,7 +527,8 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     const int b = blockIdx.y, wb = blockIdx.x;
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int k_in = a.k_in, d = a.d, nch = a.nch;
-    uint32_t* list = dyn;                         // [k_in + 64]
+    uint32_t* list = dyn;                         // [k_in + 64], then the chunks' exactness flags
+    const uint8_t* xflags = reinterpret_cast<const uint8_t*>(dyn + s1_flags_off(k_in));
     stage1_select<PX>(a, b, list, hist, sc);
 
     const long long T = (long long)a.tiles * nch;
@@ -535,13 +557,13 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         // has no exit from its middle and its loads are unconditional
         Chunk c0, c1;
         if constexpr (KIND == 1) {
-            load_chunk(list, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
+            load_chunk(list, xflags, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
             for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
-                load_chunk(list, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
+                load_chunk(list, xflags, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
                 consume_chunk_i8(c0, ag, au);
                 settle_d(ag);
                 settle_d(au);
-                load_chunk(list, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
+                load_chunk(list, xflags, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
                 consume_chunk_i8(c1, ag, au);
                 settle_d(ag);
                 settle_d(au);
@@ -562,12 +584,12 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
             const int n = ce - ca;
             const int cs0 = ca + (int)((long long)slot * n / kSlots);
             const int cs1 = ca + (int)((long long)(slot + 1) * n / kSlots);
-            load_chunk(list, k_in, cs0, cs1, crs, codes_bytes, tile_off, lane_off, c0);
+            load_chunk(list, xflags, k_in, cs0, cs1, crs, codes_bytes, tile_off, lane_off, c0);
             for (int ch = cs0; ch < cs1; ch += 2) {
-                load_chunk(list, k_in, ch + 1, cs1, crs, codes_bytes, tile_off, lane_off, c1);
+                load_chunk(list, xflags, k_in, ch + 1, cs1, crs, codes_bytes, tile_off, lane_off, c1);
                 consume_chunk_i4(c0, sgp, sup, a.p.f_pad, st, og, ou);
                 settle_d(og);
-                load_chunk(list, k_in, ch + 2, cs1, crs, codes_bytes, tile_off, lane_off, c0);
+                load_chunk(list, xflags, k_in, ch + 2, cs1, crs, codes_bytes, tile_off, lane_off, c0);
                 consume_chunk_i4(c1, sgp, sup, a.p.f_pad, st, og, ou);
                 settle_d(og);
             }
@@ -636,7 +658,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
 
 template <int KIND, int PX>
 static hipError_t go_stage1(const Stage1Args& a, int B, hipStream_t s) {
-    const size_t dyn = (size_t)(a.k_in + 64) * 4;
+    const size_t dyn = (size_t)s1_flags_off(a.k_in) * 4 + (size_t)((a.k_in + kChunk - 1) / kChunk + 16);
     auto fn = k_stage1<KIND, PX>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
