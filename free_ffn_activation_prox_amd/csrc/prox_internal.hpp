@@ -41,8 +41,13 @@ inline int stage2_blocks(int batch, int k_ff, int n_cu) {
     return w < 1 ? 1 : w;
 }
 
-// Stage-1 work split: T = tiles * nch items (tile, chunk of 8 kept inputs),
-// nb1 blocks per token.
+// Kept inputs per Stage-1 chunk (a multiple of 4).  Two chunks in flight
+// per 8-lane slot: 4 rows put 64 KB in flight per compute unit, which
+// measured faster than 8 or 12 rows (more requests only queue).
+constexpr int kChunk = 4;
+
+// Stage-1 work split: T = tiles * nch items (tile, chunk of kChunk kept
+// inputs), nb1 blocks per token.
 struct S1Geom {
     int tiles, nch, nb1;
 };
@@ -53,7 +58,7 @@ inline int s1_blocks_max(int batch) {
 inline S1Geom s1_geom(int k_in, int F, int kind, int batch, int n_cu) {
     S1Geom g;
     g.tiles = f_pad_of(F, kind) / tile_channels(kind);
-    g.nch = k_in > 0 ? (k_in + 7) / 8 : 1;
+    g.nch = k_in > 0 ? (k_in + kChunk - 1) / kChunk : 1;
     int nb = n_cu / batch;
     if (nb > s1_blocks_max(batch)) nb = s1_blocks_max(batch);
     if (nb < 1) nb = 1;

@@ -126,7 +126,7 @@ hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d,
 // ---------------------------------------------------------------------------
 // Stage 1.  grid (NB1, B), block 512 (8 waves).
 //
-// Work items: (tile, chunk) pairs, tile-major, chunk = 8 consecutive entries
+// Work items: (tile, chunk) pairs, tile-major, chunk = kChunk consecutive entries
 // of the token's kept-input list.  int8 with no more tiles than blocks: one
 // whole tile per block.  Otherwise block w takes items [w*T/NB1, (w+1)*T/NB1)
 // of the T = tiles * nch items, so every compute unit streams the same number
@@ -168,7 +168,6 @@ constexpr int kS1Threads = 512;
 // dynamic LDS: word offset
 __host__ __device__ __forceinline__ int s1_flags_off(int k_in) { return (k_in + 64 + 3) & ~3; }
 constexpr int kSlots = 64;
-constexpr int kChunk = 8;
 
 // Items [i0, i1) of block w: i0 = w * T / nb1.  The block holding item i is the
 // largest w with i0(w) <= i.  The segment of (tile, block) is stored at
@@ -210,7 +209,7 @@ __device__ __forceinline__ void stage1_score(const Stage1Args& a, int b, int j, 
     if (a.key_tap) a.key_tap[(size_t)b * a.p.F + j] = kf;
 }
 
-// One chunk of <= 8 kept rows for one lane: the packed list entries and the
+// One chunk of <= kChunk kept rows for one lane: the packed list entries and the
 // lane's 16-byte block of each tile row (buffer loads: tile offset scalar,
 // row and block offset per lane).  Entries past the segment or the list read
 // as x = 0 at an offset past the end of the codes, which the hardware returns
@@ -227,12 +226,15 @@ __device__ __forceinline__ void load_chunk(const uint32_t* list, const uint8_t* 
                                            uint32_t tile_off, uint32_t lane_off, Chunk& c) {
     const int r0 = ch * kChunk;
     const int n = ch < ch_end ? min(kChunk, k_in - r0) : 0;
-    // the 8 entries in two 16-byte LDS reads (a chunk past the list reads
-    // entries 0..7, all masked; the list has 64 spare words past k_in)
+    // the entries in 16-byte LDS reads (a chunk past the list reads the
+    // first entries, all masked; the list has 64 spare words past k_in)
     const int rr = n > 0 ? r0 : 0;
-    const uint4 ea = *reinterpret_cast<const uint4*>(list + rr);
-    const uint4 eb = *reinterpret_cast<const uint4*>(list + rr + 4);
-    const uint32_t ev[kChunk] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
+    uint32_t ev[kChunk];
+#pragma unroll
+    for (int g = 0; g < kChunk; g += 4) {
+        const uint4 e4 = *reinterpret_cast<const uint4*>(list + rr + g);
+        ev[g] = e4.x; ev[g + 1] = e4.y; ev[g + 2] = e4.z; ev[g + 3] = e4.w;
+    }
     c.exact = n > 0 ? exact[ch] != 0 : true;
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
