@@ -176,8 +176,8 @@ def alloc_workspace(d_model: int, d_ff: int, batch: int, kind: str, device="cuda
     n = workspace_bytes(d_model, d_ff, batch, kind)
     if n == 0:
         raise ValueError("invalid shape/batch for a workspace")
-    # zero-filled once: every call then leaves its histogram region at zero
-    raw = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+    # scratch: its contents on entry do not matter
+    raw = torch.empty(n + 256, dtype=torch.uint8, device=device)
     off = (-raw.data_ptr()) % 256
     return raw[off: off + n]
 

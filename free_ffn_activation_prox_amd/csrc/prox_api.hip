@@ -178,7 +178,6 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     float* key = reinterpret_cast<float*>(ws + L.key);
     float* ypart = reinterpret_cast<float*>(ws + L.ypart);
-    uint32_t* gh = reinterpret_cast<uint32_t*>(ws + L.gh);
     const int n_cu = device_cus();
     // per-token path: Stage-2 blocks on three quarters of the compute units
     // (measured faster than one per unit on the 4096 and 8192 shapes: fewer
@@ -205,18 +204,17 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
         uint16_t* hb = reinterpret_cast<uint16_t*>(ws + L.hb);
         e = launch_xsel(xb, batch, d, k_in, xm, taps ? taps->in_idx : nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "input selection");
-        // (no key histogram here: the selection ranks each token's keys itself)
         e = launch_proxy_batch(xm, batch, d, pv, reinterpret_cast<float*>(ws + L.bpart), tcnt, next_call_tag(),
                                key, taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr, s);
         if (e != hipSuccess) return hip_fail(e, "proxy GEMM");
         if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
-        e = launch_select(key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, bmask, s);
+        e = launch_select(key, batch, d, F, g.f_pad, k_ff, W2, idx, bmask, s);
         if (e != hipSuccess) return hip_fail(e, "channel selection");
         int ks = 0;
         e = launch_stage2_batch(xb, wg, wu, wd, bmask, hb, batch, d, F, g.f_pad, ypart, &ks, s);
         if (e != hipSuccess) return hip_fail(e, "stage 2 (batch)");
         if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
-        e = launch_reduce_y(ypart, batch, d, ks, y, gh, s);
+        e = launch_reduce_y(ypart, batch, d, ks, y, s);
         if (e != hipSuccess) return hip_fail(e, "reduce y");
         if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
         return PROX_OK;
@@ -224,15 +222,15 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
 
     const S1Geom g1 = s1_geom(k_in, F, p->kind, batch, n_cu);
     double* part = reinterpret_cast<double*>(ws + L.part);
-    e = launch_stage1(xb, batch, d, k_in, pv, key, gh, part, tcnt, next_call_tag(), g1,
+    e = launch_stage1(xb, batch, d, k_in, pv, key, part, tcnt, next_call_tag(), g1,
                       taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr,
                       taps ? taps->in_idx : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "stage 1");
     if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
-    e = launch_stage2(xb, wg, wu, wd, key, gh, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart, s);
+    e = launch_stage2(xb, wg, wu, wd, key, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart, s);
     if (e != hipSuccess) return hip_fail(e, "stage 2");
     if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
-    e = launch_reduce_y(ypart, batch, d, W2, y, gh, s);
+    e = launch_reduce_y(ypart, batch, d, W2, y, s);
     if (e != hipSuccess) return hip_fail(e, "reduce y");
     if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;

@@ -293,34 +293,19 @@ __device__ __forceinline__ void find_bin4(const uint32_t* hist, int krem, int* s
     lds_barrier();
 }
 
-// The coarse digit from a histogram built outside the block: NB bins of
-// key >> shift over the n valid keys, in global memory.  On success st holds
-// the threshold bin (prefix), `above` = keys in higher bins and krem = k -
-// above.  Returns false when the bins do not add up to n, i.e. the histogram
-// is not the one of these keys; the caller then ranks without it.
-// Requires 1 <= k <= n.
-// This thread's bins of a histogram in global memory, as block_hist_bin_regs
-// takes them: c[i] = bin NB - (t + 1) * PER + i (16-byte loads).
-template <int NT, int NB>
-__device__ __forceinline__ void load_hist_bins(const uint32_t* __restrict__ gh, uint32_t (&c)[NB / NT]) {
-    constexpr int PER = NB / NT;
-    static_assert(PER % 4 == 0 && PER * NT == NB, "16-byte loads of whole bins");
-    const uint4* src = reinterpret_cast<const uint4*>(gh + NB - ((int)threadIdx.x + 1) * PER);
-#pragma unroll
-    for (int v = 0; v < PER / 4; ++v) {
-        const uint4 u = src[v];
-        c[4 * v] = u.x; c[4 * v + 1] = u.y; c[4 * v + 2] = u.z; c[4 * v + 3] = u.w;
-    }
-}
-
-// block_hist_bin with this thread's bins already in registers (load_hist_bins).
+// The coarse digit from a histogram of the n valid keys: NB bins of
+// key >> shift, thread t holding bins NB - (t + 1) * PER + i in c[i].  On
+// success st holds the threshold bin (prefix), `above` = keys in higher bins
+// and krem = k - above.  Returns false when the bins do not add up to n
+// (a bin out of range, or a total that differs); the caller then ranks
+// without them.  Requires 1 <= k <= n.
 template <int NT, int NB>
 __device__ __forceinline__ bool block_hist_bin_regs(const uint32_t (&c)[NB / NT], int k, int n, int shift, int* sc,
                                                     SelectState& st) {
     constexpr int PER = NB / NT;
-    // A stale histogram may hold anything.  Bins are checked one by one, so a
-    // thread's contribution is its true sum (no wrap) or n + 1; the block
-    // total is n exactly when no bin is out of range and the bins add up.
+    // Bins are checked one by one, so a thread's contribution is its true sum
+    // (no wrap) or n + 1; the block total is n exactly when no bin is out of
+    // range and the bins add up.
     uint32_t mine = 0;
     bool bad = false;
 #pragma unroll
@@ -346,17 +331,9 @@ __device__ __forceinline__ bool block_hist_bin_regs(const uint32_t (&c)[NB / NT]
     return true;
 }
 
-template <int NT, int NB>
-__device__ __forceinline__ bool block_hist_bin(const uint32_t* __restrict__ gh, int k, int n, int shift, int* sc,
-                                               SelectState& st) {
-    uint32_t c[NB / NT];
-    load_hist_bins<NT, NB>(gh, c);
-    return block_hist_bin_regs<NT, NB>(c, k, n, shift, sc, st);
-}
-
 // The coarse digit from the block's own keys: one radix digit of <= 11 bits
 // in a window that starts at the highest bit set in any key (keys < 2^nbits).
-// Same outputs as block_hist_bin.  Requires 1 <= k <= number of valid keys.
+// Same outputs as block_hist_bin_regs.  Requires 1 <= k <= number of valid keys.
 template <int P, int NT>
 __device__ __forceinline__ SelectState block_coarse_bin(const uint32_t (&key)[P], const bool (&valid)[P], int k,
                                         int nbits, uint32_t* hist, int* sc) {

@@ -12,11 +12,16 @@ constexpr int kTileRowBytes = 128;   // bytes of one tile row of the proxy (one 
 constexpr int kMaxW2Total = 512;     // upper bound on Stage-2 blocks per launch (all tokens)
 constexpr int kMaxS1Total = 512;     // upper bound on Stage-1 blocks per launch (all tokens)
 constexpr int kPartChannels = 128;   // channels per partial-sum slot (the int4 tile width)
-// Coarse histogram of the ranking keys that Stage 1 builds per token: the bin
-// of a key is its fp32 bit pattern >> 18 (keys are >= 0, so 13 bits: sign 0,
-// exponent, 5 mantissa bits; 32 bins per binade).
+// Coarse histogram of the ranking keys that each Stage-2 block builds in LDS
+// for its token: the bin of a key is its fp32 bit pattern >> 18 (keys are
+// >= 0, so 13 bits: sign 0, exponent, 5 mantissa bits; 32 bins per binade).
 constexpr int kGhShift = 18;
 constexpr int kGhBins = 1 << (31 - kGhShift);
+// Stage-2 LDS words holding the histogram, then (slow paths) every key of F.
+inline __host__ __device__ int s2_keys_words(int F) {
+    const int kw = (F + 64 + 3) & ~3;
+    return kw > kGhBins ? kw : kGhBins;
+}
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int tile_channels(int kind) { return kind == 1 ? 64 : 128; }
@@ -96,7 +101,7 @@ DnSplit down_batch_split(int B, int d, int F);
 // Workspace carve-up (byte offsets) for one (d, F, B, kind).  The batch
 // regions (xm, bpart, bmask, hb) are empty below kBatchMin tokens.
 struct WsLayout {
-    size_t key, ypart, gh, part, tcnt, xm, bpart, bmask, hb, total;
+    size_t key, ypart, part, tcnt, xm, bpart, bmask, hb, total;
 };
 inline WsLayout ws_layout(int d, int F, int B, int kind) {
     const int fp = f_pad_of(F, kind);
@@ -106,7 +111,6 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
     size_t o = 0;
     L.key = o;    o = align_up(o + (size_t)B * fp * 4, 256);
     L.ypart = o;  o = align_up(o + (size_t)B * stage2_blocks_max(B) * d * 4, 256);
-    L.gh = o;     o = align_up(o + (size_t)B * kGhBins * 4, 256);
     L.part = o;   o = align_up(o + (size_t)B * (fp / tile_channels(kind) + s1_blocks_max(B)) * 2 * kPartChannels * 8, 256);
     L.tcnt = o;   o = align_up(o + (size_t)B * (fp / tile_channels(kind)) * 8, 256);
     L.xm = o;     o = align_up(o + (batch ? (size_t)B * d * 2 : 0), 256);
@@ -121,18 +125,16 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
 hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d, int F,
                               const ProxyView& p, hipStream_t s);
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
-                         uint32_t* gh, double* part, unsigned long long* tcnt, uint32_t gen,
+                         double* part, unsigned long long* tcnt, uint32_t gen,
                          const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
                          hipStream_t s);
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
-                         const uint16_t* wd, const float* key, const uint32_t* gh, int B, int d,
-                         int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask,
-                         float* ypart, hipStream_t s);
-hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, uint32_t* gh,
-                           hipStream_t s);
+                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
+                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, hipStream_t s);
+hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s);
 // Stage-2 selection only: mask (required) and idx (nullable) from the keys.
-hipError_t launch_select(const float* key, const uint32_t* gh, int B, int d, int F, int f_pad, int k_ff,
-                         int W2, int32_t* idx, uint8_t* mask, hipStream_t s);
+hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
+                         int32_t* idx, uint8_t* mask, hipStream_t s);
 
 // ---- batch launchers (prox_batch.hip)
 hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,

@@ -5,10 +5,9 @@
 //            every block: x is a few KB), then the block's equal share of the
 //            (channel tile, kept-row chunk) items of the proxy GEMV
 //   score    per (channel tile, token): the tile's partial sums in a fixed
-//            order, h~ = silu(g~) u~ in fp64, the fp32 ranking key |h~| and a
-//            coarse histogram of the keys
-//   stage2   per (block, token): top-k of the keys (threshold bin from the
-//            histogram, redone in every block), the block's share of the kept
+//            order, h~ = silu(g~) u~ in fp64 and the fp32 ranking key |h~|
+//   stage2   per (block, token): top-k of the keys (threshold bin from a
+//            coarse LDS histogram, redone in every block), the block's share of the kept
 //            channels, then for each of them the exact gate/up dots over the
 //            dense x, h = silu(g) u and h * W_down row into the block's partial y
 //   reduce   y = fixed-order sum of the block partials
@@ -153,7 +152,6 @@ struct Stage1Args {
     int d, k_in;
     ProxyView p;
     float* key;          // [B][f_pad]
-    uint32_t* gh;        // [B][kGhBins] coarse key histogram (zero on entry)
     double* part;        // [B][tiles + nb1][2][128] segment partial sums
     unsigned long long* tcnt;   // [B][tiles] arrival counters: call tag << 32 | arrivals
     double* h_tap;       // [B][F] or null
@@ -191,8 +189,8 @@ __device__ __forceinline__ int s1_arrive(unsigned long long* cnt, uint32_t gen, 
     }
 }
 
-// h~ = silu(g~) u~ in fp64 (int8: per-channel scales applied here), the fp32
-// ranking key |h~| and its coarse histogram bin.
+// h~ = silu(g~) u~ in fp64 (int8: per-channel scales applied here) and the
+// fp32 ranking key |h~|.
 __device__ __forceinline__ void stage1_score(const Stage1Args& a, int b, int j, double g, double u,
                                              float sg, float su) {
     if (j >= a.p.F) return;
@@ -203,8 +201,6 @@ __device__ __forceinline__ void stage1_score(const Stage1Args& a, int b, int j, 
     const double h = g / (1.0 + exp(-g)) * u;
     const float kf = (float)fabs(h);
     a.key[(size_t)b * a.p.f_pad + j] = kf;
-    __hip_atomic_fetch_add(a.gh + (size_t)b * kGhBins + (__float_as_uint(kf) >> kGhShift), 1u,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.h_tap) a.h_tap[(size_t)b * a.p.F + j] = h;
     if (a.key_tap) a.key_tap[(size_t)b * a.p.F + j] = kf;
 }
@@ -680,10 +676,10 @@ static hipError_t stage1_px(const Stage1Args& a, int B, hipStream_t s) {
 }
 
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
-                         uint32_t* gh, double* part, unsigned long long* tcnt, uint32_t gen,
+                         double* part, unsigned long long* tcnt, uint32_t gen,
                          const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
                          hipStream_t s) {
-    Stage1Args a{x, d, k_in, p, key, gh, part, tcnt, h_tap, key_tap, in_idx_tap, g.tiles, g.nch, g.nb1, gen};
+    Stage1Args a{x, d, k_in, p, key, part, tcnt, h_tap, key_tap, in_idx_tap, g.tiles, g.nch, g.nb1, gen};
     return p.kind == 1 ? stage1_px<1>(a, B, s) : stage1_px<2>(a, B, s);
 }
 
@@ -705,7 +701,6 @@ struct Stage2Args {
     const uint16_t* wu_t;
     const uint16_t* wd;
     const float* key;     // [B][f_pad]
-    const uint32_t* gh;   // [B][kGhBins] key histogram from Stage 1
     int d, F, f_pad, k, W2;
     int32_t* idx;         // [B][k] or null
     uint8_t* mask;        // [B][F] or null
@@ -820,8 +815,9 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
 // ---------------------------------------------------------------------------
 // Stage 2 top-k.  A threshold bin (prefix at shift) splits the keys: those in
 // higher bins are kept for certain ("certain"), those in the bin are
-// "candidates".  The bin comes from the histogram Stage 1 built (else from the
-// block's own keys).  Thread t owns channels t*PK .. t*PK + PK - 1 for the
+// "candidates".  The bin comes from a histogram of the keys' top 13 bits that
+// the block builds in LDS (should its bins not add up, from a radix digit of
+// the block's own keys).  Thread t owns channels t*PK .. t*PK + PK - 1 for the
 // block-wide counts; the candidates go to LDS in index order and each gets
 // its rank (key descending, index ascending), so a candidate is kept when its
 // rank is below k - (certain keys).  The block's own range is handled one
@@ -851,8 +847,8 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int F = a.F, k = a.k, W2 = a.W2;
     const int r0 = (int)((long long)w * F / W2), r1 = (int)((long long)(w + 1) * F / W2);
     const int L = r1 - r0;                                 // channels of this block's range
-    uint32_t* keys = dyn2;                                 // [F + 64, to 16 B] every key, index order
-    uint32_t* cval = keys + ((F + 64 + 3) & ~3);           // [kCandCap + 64] candidate keys, index order
+    uint32_t* keys = dyn2;                                 // [s2_keys_words(F)] the key histogram, then every key (index order)
+    uint32_t* cval = keys + s2_keys_words(F);              // [kCandCap + 64] candidate keys, index order
     uint16_t* cidx = reinterpret_cast<uint16_t*>(cval + kCandCap + 64);   // [kCandCap + 64] their channels
     uint16_t* kr = cidx + kCandCap + 64;                   // [kCandCap] rank among the kept candidates
     uint16_t* chan = kr + kCandCap;                        // [cap + 64] the block's list
@@ -876,13 +872,17 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
     }
-    // keys and the key histogram's bins, requested together
+    const bool all = k >= F, none = k == 0;
+    // the keys, and the histogram of their high bits cleared meanwhile
     uint32_t kb[PK];
-    uint32_t cbin[kGhBins / NT];
     {
         bool valid[PK];
         load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
-        load_hist_bins<NT, kGhBins>(a.gh + (size_t)b * kGhBins, cbin);
+        if (!all && !none) {
+#pragma unroll
+            for (int v = 0; v < kGhBins / NT / 4; ++v)
+                reinterpret_cast<uint4*>(keys)[v * NT + t] = make_uint4(0u, 0u, 0u, 0u);
+        }
         // keys past F: negative as int, below every bin of a valid key
 #pragma unroll
         for (int q = 0; q < PK; ++q) kb[q] = valid[q] ? kb[q] : 0x80000000u;
@@ -900,10 +900,26 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const uint32_t own0 = t < L ? __float_as_uint(keyb[r0 + t]) : 0u;
     if (STREAM && t == 0) chan[0] = 0;                     // row 0 stands in for an empty list
 
-    // ---- threshold bin
-    const bool all = k >= F, none = k == 0;
+    // ---- threshold bin: the block's key histogram (every key's top bits;
+    // a key is a non-negative float, so its bit pattern orders like its
+    // value), this thread's bins NB - 16 (t + 1) .. read back as 16-byte words
     SelectState st{0u, 0, 0, 0, 0};
     if (!all && !none) {
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < PK; ++q)
+            if ((int)kb[q] >= 0) atomicAdd(&keys[kb[q] >> kGhShift], 1u);
+        lds_barrier();
+        uint32_t cbin[kGhBins / NT];
+        {
+            const uint4* src = reinterpret_cast<const uint4*>(keys + kGhBins - (t + 1) * (kGhBins / NT));
+#pragma unroll
+            for (int v = 0; v < kGhBins / NT / 4; ++v) {
+                const uint4 u = src[v];
+                cbin[4 * v] = u.x; cbin[4 * v + 1] = u.y; cbin[4 * v + 2] = u.z; cbin[4 * v + 3] = u.w;
+            }
+        }
+        // (the scans below hold barriers before keys_to_lds overwrites the histogram)
         if (!block_hist_bin_regs<NT, kGhBins>(cbin, k, F, kGhShift, sc, st)) {
             bool valid[PK];
 #pragma unroll
@@ -1148,7 +1164,7 @@ template <int PK, int R, int G, bool STREAM>
 static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     // list length bound: ceil(C/W2) + ceil(KC/W2); selection only keeps no list
     const int cap = STREAM ? (a.k + a.W2 - 1) / a.W2 + 2 : 0;
-    const size_t dyn = ((size_t)(a.F + 64 + 3) & ~(size_t)3) * 4 + ((size_t)kCandCap + 64) * 4 +
+    const size_t dyn = (size_t)s2_keys_words(a.F) * 4 + ((size_t)kCandCap + 64) * 4 +
                        ((size_t)kCandCap * 2 + 64 + cap + 64) * 2;
     auto fn = k_stage2<PK, R, G, STREAM>;
     if (dyn > 48 * 1024) {
@@ -1174,10 +1190,9 @@ static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
 }
 
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
-                         const uint16_t* wd, const float* key, const uint32_t* gh, int B, int d,
-                         int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask,
-                         float* ypart, hipStream_t s) {
-    Stage2Args a{x, wg_t, wu_t, wd, key, gh, d, F, f_pad, k_ff, W2, idx, mask, ypart};
+                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
+                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, hipStream_t s) {
+    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart};
     // channels per group: the fewest that keep the stream at its rate (more
     // rows in flight per block measured slower on the 4096 and 8192 shapes)
     if (d <= 4096) return stage2_pk<1, 2, true>(a, B, s);
@@ -1185,15 +1200,14 @@ hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t
     return stage2_pk<4, 1, true>(a, B, s);
 }
 
-hipError_t launch_select(const float* key, const uint32_t* gh, int B, int d, int F, int f_pad, int k_ff,
-                         int W2, int32_t* idx, uint8_t* mask, hipStream_t s) {
-    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, gh, d, F, f_pad, k_ff, W2, idx, mask, nullptr};
+hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
+                         int32_t* idx, uint8_t* mask, hipStream_t s) {
+    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr};
     return stage2_pk<1, 1, false>(a, B, s);
 }
 
 // ---------------------------------------------------------------------------
-// y = sum of the W2 block partials, fixed order, and the token's key
-// histogram back to zero for the next call.  grid (ceil(d / 16), B), block
+// y = sum of the W2 block partials, fixed order.  grid (ceil(d / 16), B), block
 // 256: thread (g = t / 4, c = t % 4) sums partials g, g + 64, ... of columns
 // 4c .. 4c + 3 of the block's 16 (all of its loads in flight at once), then
 // the 64 groups are combined in LDS in a fixed tree.
@@ -1203,7 +1217,7 @@ constexpr int kRedGroups = 64;
 constexpr int kRedMax = kMaxW2Total / kRedGroups;   // partials per thread
 
 __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypart, int d, int W2,
-                                                  float* __restrict__ y, uint32_t* __restrict__ gh) {
+                                                  float* __restrict__ y) {
     __shared__ float4 acc[kRedGroups][kRedCols / 4];
     const int b = blockIdx.y, t = threadIdx.x;
     const int g = t >> 2, c = t & 3;
@@ -1233,16 +1247,11 @@ __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypar
         __syncthreads();
     }
     if (g == 0 && in) *reinterpret_cast<float4*>(y + (size_t)b * d + col) = s4;
-    // histogram: this token's bins, spread over the token's blocks
-    uint32_t* hb = gh + (size_t)b * kGhBins;
-    for (int i = (blockIdx.x * 256 + t) * 4; i < kGhBins; i += gridDim.x * 256 * 4)
-        *reinterpret_cast<uint4*>(hb + i) = make_uint4(0, 0, 0, 0);
 }
 
-hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, uint32_t* gh,
-                           hipStream_t s) {
+hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s) {
     hipLaunchKernelGGL(k_reduce_y, dim3((d + kRedCols - 1) / kRedCols, B), dim3(256), 0, s, ypart, d,
-                       W2, y, gh);
+                       W2, y);
     return hipGetLastError();
 }
 

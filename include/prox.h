@@ -157,11 +157,8 @@ size_t prox_workspace_bytes(int32_t d_model, int32_t d_ff, int32_t batch, int32_
  *   mask   device uint8 [batch][d_ff] 0/1, nullable
  *   idx    device int32 [batch][k_ff] kept channels ascending, nullable
  *   workspace  device, >= prox_workspace_bytes(d_model, d_ff, batch, kind),
- *          256-byte aligned, zero-filled before its first use.  Each call
- *          leaves it ready for the next one (a per-token histogram region
- *          is returned to zero); the rest is scratch.  A workspace that was
- *          not zero-filled still gives exact results: the call detects the
- *          stale histogram and ranks without it, more slowly.  Calls that
+ *          256-byte aligned.  Scratch only: its contents on entry do not
+ *          change the result, and it need not be cleared.  Calls that
  *          share a workspace must not overlap in time.                    */
 prox_status prox_ffn_forward(const void* x, int32_t batch, const prox_weights* w,
                              const prox_proxy* p, int32_t k_in, int32_t k_ff, float* y,

@@ -116,9 +116,8 @@ def test_repeatable():
 
 
 def test_stale_workspace_still_exact():
-    # The key histogram region must be zero on entry; a workspace holding
-    # anything else is detected and ranked without it (same mask and idx), and
-    # the call leaves the region zeroed, so the next call matches bit for bit.
+    # The workspace is scratch: whatever it holds on entry (the Stage-1
+    # arrival counters included), the call gives the same outputs bit for bit.
     c = _case(1024, 2000, 3, seed=11, kind="int8")
     import free_ffn_activation_prox_amd as P
     ws = P.alloc_workspace(1024, 2000, 3, "int8")
@@ -130,8 +129,7 @@ def test_stale_workspace_still_exact():
         else:
             ws.copy_(torch.from_numpy(noise).to(ws.device))
         y, m, i = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 700, workspace=ws)
-        assert torch.equal(m, ref[1]) and torch.equal(i, ref[2]), fill
-        assert (y - ref[0]).abs().max().item() <= 1e-5 * ref[0].abs().max().item(), fill
+        assert torch.equal(m, ref[1]) and torch.equal(i, ref[2]) and torch.equal(y, ref[0]), fill
         again = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 700, workspace=ws)
         for u, v in zip(again, ref):
             assert torch.equal(u, v), fill
