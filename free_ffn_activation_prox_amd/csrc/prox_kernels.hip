@@ -858,17 +858,14 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const uint32_t mat_bytes = (uint32_t)F * row_bytes;
     const RowRsrc rs{make_rsrc(a.wg_t, mat_bytes), make_rsrc(a.wu_t, mat_bytes), make_rsrc(a.wd, mat_bytes)};
     uint32_t voff[R];
-    float xr[R][8], yacc[R][8];
+    uint4 xv[R];                    // this thread's 8 x values per row part, as loaded (converted
+    float yacc[R][8];               // when the stream starts: nothing before it waits for them)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int col = r * 4096 + t * 8;
         voff[r] = col < a.d ? (uint32_t)col * 2u : mat_bytes;   // past d: read as zeros
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (STREAM && col < a.d) v = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
-        xr[r][0] = bf16_lo(v.x); xr[r][1] = bf16_hi(v.x);
-        xr[r][2] = bf16_lo(v.y); xr[r][3] = bf16_hi(v.y);
-        xr[r][4] = bf16_lo(v.z); xr[r][5] = bf16_hi(v.z);
-        xr[r][6] = bf16_lo(v.w); xr[r][7] = bf16_hi(v.w);
+        xv[r] = make_uint4(0, 0, 0, 0);
+        if (STREAM && col < a.d) xv[r] = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
     }
@@ -1135,6 +1132,14 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     // loaded past the list (zeros, no memory access) and left unused.
     const int rest = n - E;
     const int groups = 1 + (rest + G - 1) / G;
+    float xr[R][8];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        xr[r][0] = bf16_lo(xv[r].x); xr[r][1] = bf16_hi(xv[r].x);
+        xr[r][2] = bf16_lo(xv[r].y); xr[r][3] = bf16_hi(xv[r].y);
+        xr[r][4] = bf16_lo(xv[r].z); xr[r][5] = bf16_hi(xv[r].z);
+        xr[r][6] = bf16_lo(xv[r].w); xr[r][7] = bf16_hi(xv[r].w);
+    }
     int gi = 0;
     for (; gi + 1 < groups; gi += 2) {
         load_group<R, G>(rs, chan, E + gi * G, n, row_bytes, mat_bytes, voff, nxt);
