@@ -1141,6 +1141,18 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         xr[r][6] = bf16_lo(xv[r].w); xr[r][7] = bf16_hi(xv[r].w);
     }
     int gi = 0;
+    if (groups >= 2) {
+        // the first two groups: the mask and idx of the block's range are
+        // written while both are in flight
+        load_group<R, G>(rs, chan, E, n, row_bytes, mat_bytes, voff, nxt);
+        write_range();
+        consume_group<R, G>(cur, xr, yacc, E, red[0]);
+        settle(yacc);
+        load_group<R, G>(rs, chan, E + G, n, row_bytes, mat_bytes, voff, cur);
+        consume_group<R, G>(nxt, xr, yacc, min(G, rest), red[1]);
+        settle(yacc);
+        gi = 2;
+    }
     for (; gi + 1 < groups; gi += 2) {
         load_group<R, G>(rs, chan, E + gi * G, n, row_bytes, mat_bytes, voff, nxt);
         consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
@@ -1153,7 +1165,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         settle(yacc);
     }
     if (gi < groups) consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
-    write_range();
+    if (groups < 2) write_range();
     float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
