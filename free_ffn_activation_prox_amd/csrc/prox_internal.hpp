@@ -17,10 +17,11 @@ constexpr int kPartChannels = 128;   // channels per partial-sum slot (the int4 
 // >= 0, so 13 bits: sign 0, exponent, 5 mantissa bits; 32 bins per binade).
 constexpr int kGhShift = 18;
 constexpr int kGhBins = 1 << (31 - kGhShift);
-// Stage-2 LDS words holding the histogram, then (slow paths) every key of F.
+// Stage-2 LDS words holding the histogram (and 64 spare bins for keys past
+// F), then (slow paths) every key of F.
 inline __host__ __device__ int s2_keys_words(int F) {
     const int kw = (F + 64 + 3) & ~3;
-    return kw > kGhBins ? kw : kGhBins;
+    return kw > kGhBins + 64 ? kw : kGhBins + 64;
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -880,9 +880,10 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             for (int v = 0; v < kGhBins / NT / 4; ++v)
                 reinterpret_cast<uint4*>(keys)[v * NT + t] = make_uint4(0u, 0u, 0u, 0u);
         }
-        // keys past F: negative as int, below every bin of a valid key
+        // keys past F: negative as int, below every bin of a valid key; their
+        // histogram bin (kGhBins + lane) is a spare word, one per lane
 #pragma unroll
-        for (int q = 0; q < PK; ++q) kb[q] = valid[q] ? kb[q] : 0x80000000u;
+        for (int q = 0; q < PK; ++q) kb[q] = valid[q] ? kb[q] : 0x80000000u | ((uint32_t)(t & 63) << kGhShift);
     }
     // every key in LDS too (index order), for the slow paths (written after
     // the candidate count is known)
@@ -903,9 +904,10 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     SelectState st{0u, 0, 0, 0, 0};
     if (!all && !none) {
         lds_barrier();
+        // keys past F land in the spare bins past the histogram (never read),
+        // one per lane so they do not contend: no branch per key
 #pragma unroll
-        for (int q = 0; q < PK; ++q)
-            if ((int)kb[q] >= 0) atomicAdd(&keys[kb[q] >> kGhShift], 1u);
+        for (int q = 0; q < PK; ++q) atomicAdd(&keys[min(kb[q] >> kGhShift, (uint32_t)(kGhBins + 63))], 1u);
         lds_barrier();
         uint32_t cbin[kGhBins / NT];
         {
