@@ -363,16 +363,20 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         }
     }
     lds_barrier();
-    // each chunk's exactness flag (entries past k_in are empty)
-    uint8_t* exact = reinterpret_cast<uint8_t*>(list + s1_flags_off(k_in));
+}
+
+// Each chunk's exactness flag (entries past k_in are empty), into LDS after
+// the list.  The caller issues its first chunk loads before this and holds a
+// barrier after it.
+__device__ __forceinline__ void stage1_flags(const uint32_t* list, int k_in) {
+    uint8_t* exact = reinterpret_cast<uint8_t*>(const_cast<uint32_t*>(list) + s1_flags_off(k_in));
     const int nch = (k_in + kChunk - 1) / kChunk;
-    for (int ch = t; ch < nch; ch += NT) {
+    for (int ch = threadIdx.x; ch < nch; ch += kS1Threads) {
         Chunk c;
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) c.e[u] = ch * kChunk + u < k_in ? list[ch * kChunk + u] : 0u;
         exact[ch] = chunk_exact32(c) ? 1 : 0;
     }
-    lds_barrier();
 }
 
 // Unsigned byte c of w as float (one conversion instruction).
@@ -528,6 +532,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     uint32_t* list = dyn;                         // [k_in + 64], then the chunks' exactness flags
     const uint8_t* xflags = reinterpret_cast<const uint8_t*>(dyn + s1_flags_off(k_in));
     stage1_select<PX>(a, b, list, hist, sc);
+    bool flags_done = false;     // the chunk flags are computed under the block's first loads
 
     const long long T = (long long)a.tiles * nch;
     const long long i0 = s1_item0(wb, T, a.nb1), i1 = s1_item0(wb + 1, T, a.nb1);
@@ -556,6 +561,12 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         Chunk c0, c1;
         if constexpr (KIND == 1) {
             load_chunk(list, xflags, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
+            if (!flags_done) {
+                stage1_flags(list, k_in);
+                lds_barrier();
+                flags_done = true;
+                c0.exact = ca + slot < ce ? xflags[ca + slot] != 0 : true;
+            }
             for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
                 load_chunk(list, xflags, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
                 consume_chunk_i8(c0, ag, au);
@@ -583,6 +594,12 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
             const int cs0 = ca + (int)((long long)slot * n / kSlots);
             const int cs1 = ca + (int)((long long)(slot + 1) * n / kSlots);
             load_chunk(list, xflags, k_in, cs0, cs1, crs, codes_bytes, tile_off, lane_off, c0);
+            if (!flags_done) {
+                stage1_flags(list, k_in);
+                lds_barrier();
+                flags_done = true;
+                c0.exact = cs0 < cs1 ? xflags[cs0] != 0 : true;
+            }
             for (int ch = cs0; ch < cs1; ch += 2) {
                 load_chunk(list, xflags, k_in, ch + 1, cs1, crs, codes_bytes, tile_off, lane_off, c1);
                 consume_chunk_i4(c0, sgp, sup, a.p.f_pad, st, og, ou);
