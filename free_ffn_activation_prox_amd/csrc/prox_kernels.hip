@@ -1245,8 +1245,9 @@ hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k
 // ---------------------------------------------------------------------------
 // y = sum of the W2 block partials, fixed order.  grid (ceil(d / 16), B), block
 // 256: thread (g = t / 4, c = t % 4) sums partials g, g + 64, ... of columns
-// 4c .. 4c + 3 of the block's 16 (all of its loads in flight at once), then
-// the 64 groups are combined in LDS in a fixed tree.
+// 4c .. 4c + 3 of the block's 16 (all of its loads in flight at once); the 16
+// groups of a wave are combined by lane swaps (lanes 4 apart, then 8, 16, 32),
+// the 4 waves through LDS, in a fixed order.
 // ---------------------------------------------------------------------------
 constexpr int kRedCols = 16;
 constexpr int kRedGroups = 64;
@@ -1254,7 +1255,7 @@ constexpr int kRedMax = kMaxW2Total / kRedGroups;   // partials per thread
 
 __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypart, int d, int W2,
                                                   float* __restrict__ y) {
-    __shared__ float4 acc[kRedGroups][kRedCols / 4];
+    __shared__ float4 acc[4][kRedCols / 4];
     const int b = blockIdx.y, t = threadIdx.x;
     const int g = t >> 2, c = t & 3;
     const int col = blockIdx.x * kRedCols + 4 * c;
@@ -1271,18 +1272,25 @@ __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypar
     for (int u = 1; u < kRedMax; ++u) {
         s4.x += v[u].x; s4.y += v[u].y; s4.z += v[u].z; s4.w += v[u].w;
     }
-    acc[g][c] = s4;
-    __syncthreads();
 #pragma unroll
-    for (int h = kRedGroups / 2; h >= 1; h >>= 1) {
-        if (g < h) {
-            const float4 o = acc[g + h][c];
-            s4.x += o.x; s4.y += o.y; s4.z += o.z; s4.w += o.w;
-            acc[g][c] = s4;
-        }
-        __syncthreads();
+    for (int m = 4; m < kWave; m <<= 1) {
+        s4.x += __shfl_xor(s4.x, m, kWave);
+        s4.y += __shfl_xor(s4.y, m, kWave);
+        s4.z += __shfl_xor(s4.z, m, kWave);
+        s4.w += __shfl_xor(s4.w, m, kWave);
     }
-    if (g == 0 && in) *reinterpret_cast<float4*>(y + (size_t)b * d + col) = s4;
+    const int wv = t / kWave;
+    if ((t & (kWave - 1)) < 4) acc[wv][c] = s4;
+    __syncthreads();
+    if (t < 4 && in) {
+        float4 r = acc[0][c];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            const float4 o = acc[q][c];
+            r.x += o.x; r.y += o.y; r.z += o.z; r.w += o.w;
+        }
+        *reinterpret_cast<float4*>(y + (size_t)b * d + col) = r;
+    }
 }
 
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s) {
