@@ -179,10 +179,11 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     float* key = reinterpret_cast<float*>(ws + L.key);
     float* ypart = reinterpret_cast<float*>(ws + L.ypart);
     const int n_cu = device_cus();
-    // per-token path: Stage-2 blocks on three quarters of the compute units
-    // (measured faster than one per unit on the 4096 and 8192 shapes: fewer
-    // concurrent row streams, fewer partial outputs to add)
-    const int W2 = stage2_blocks(batch, k_ff, batch >= kBatchMin ? n_cu : n_cu * 3 / 4);
+    // per-token path: Stage-2 blocks on every compute unit up to d_model 4096,
+    // on three quarters of them above (measured, µs per token: c2_s70 44.8 at
+    // 256 blocks against 45.2 at 192; c4_b1_s70 152.3 at 192 against 153.8 at
+    // 256, whose longer rows keep more bytes in flight per block)
+    const int W2 = stage2_blocks(batch, k_ff, batch >= kBatchMin || d <= 4096 ? n_cu : n_cu * 3 / 4);
 
     void* const* ev = (taps && taps->events && taps->n_events >= PROX_N_PHASES + 1) ? taps->events : nullptr;
     auto mark = [&](int i) -> hipError_t {
