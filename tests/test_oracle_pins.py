@@ -402,3 +402,197 @@ def test_mutant_down_transposed(monkeypatch):
     orig = O.stage2_token
     monkeypatch.setattr(O, "stage2_token", lambda x, wg, wu, wd, m: orig(x, wg, wu, np.ascontiguousarray(wd.T), m))
     assert _caught(lambda: check_dense_identity("int8", 64, 64, 1, 32, 0))
+
+
+# ---------------------------------------------------------------------------
+# P7. bf16 bit patterns -> values, from the format's definition (bf16 is the
+# top 16 bits of an IEEE binary32: 1 sign, 8 exponent, 7 fraction bits).
+# ---------------------------------------------------------------------------
+
+def test_p7_bf16_bits_hand_values():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x0001, 0x007F, 0x0080, 0x7F7F, 0x7F80, 0x3EAB],
+                    dtype=np.uint16)
+    v = O.bf16_bits_to_f64(bits)
+    assert v.dtype == np.float64
+    assert v[0] == 1.0 and v[1] == -2.0
+    assert v[2] == 0.0 and not np.signbit(v[2])
+    assert v[3] == 0.0 and np.signbit(v[3])                      # -0 keeps its sign
+    assert v[4] == 2.0 ** -133                                    # smallest subnormal: 1 * 2^(-126 - 7)
+    assert v[5] == 127 * 2.0 ** -133                              # largest subnormal
+    assert v[6] == 2.0 ** -126                                    # smallest normal
+    assert v[7] == (1 + 127 / 128) * 2.0 ** 127                   # largest finite bf16
+    assert np.isinf(v[8]) and v[8] > 0
+    assert v[9] == (1 + 0x2B / 128) * 2.0 ** (0x7D - 127)         # 0x3EAB: exponent 125, fraction 43
+    # 2-D input keeps its shape
+    assert O.bf16_bits_to_f64(bits.reshape(2, 5)).shape == (2, 5)
+
+
+# ---------------------------------------------------------------------------
+# P8. int4 group-128 proxy with several groups: every W~[i, j] is the scalar
+# product of the scale of row i's group, s[i // 128, j], and the code q[i, j];
+# brute force over the channel subsets on a two-group input (d = 256).
+# ---------------------------------------------------------------------------
+
+def check_int4_two_groups(seed, d=256, F=7, k_in=150, k_ff=3):
+    x, wg, wu, wd = _case(d, F, 1, seed)
+    # give the two groups very different scales so a wrong group is visible
+    wg[:, 128:] *= 8.0
+    wu[:, :128] *= 0.25
+    res = O.oracle_forward(x, wg, wu, wd, "int4", k_in, k_ff)
+    tok = res.tokens[0]
+    pg, pu = O.build_proxy(wg.T, "int4"), O.build_proxy(wu.T, "int4")
+    for p in (pg, pu):
+        assert p.s.shape == (d // 128, F)
+        for i in range(0, d, 37):
+            for j in range(F):
+                assert p.w_tilde[i, j] == float(p.s[i // 128, j]) * float(p.q[i, j]), (i, j)
+    order = sorted(range(d), key=lambda i: (-abs(x[0, i]), i))[:k_in]
+    assert list(tok.s_in) == sorted(order)
+    keys = []
+    for j in range(F):
+        gh = math.fsum(float(x[0, i]) * float(pg.s[i // 128, j]) * float(pg.q[i, j]) for i in order)
+        uh = math.fsum(float(x[0, i]) * float(pu.s[i // 128, j]) * float(pu.q[i, j]) for i in order)
+        hh = _silu_scalar(gh) * uh
+        assert abs(hh - tok.h_hat[j]) <= 1e-12 * abs(hh) + 1e-300, j
+        keys.append(float(np.float32(abs(hh))))
+    assert list(tok.mask) == _brute_select(keys, k_ff)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_p8_int4_two_groups(seed):
+    check_int4_two_groups(seed)
+
+
+# ---------------------------------------------------------------------------
+# P9. The threshold t is |h~| of the k-th channel in the ranking (the last one
+# kept), not of the first one dropped.  Hand example of P6: |h~| ranks
+# channels 0, 1, 3, 2, so with k = 2 the threshold is |h~_1|; with k = 1 it
+# is |h~_0|; with k = F it is the smallest, |h~_2|.
+# ---------------------------------------------------------------------------
+
+def check_threshold_hand():
+    wg_t, wu_t = (QG / 128).T, (QU / 128).T
+    sil = lambda z: z / (1 + math.exp(-z))  # noqa: E731
+    hh = [abs(sil(a / 128) * b / 128) for a, b in ((246, 132), (-4, 294), (-60, -20), (2, 512))]
+    for k, j in ((1, 0), (2, 1), (3, 3), (4, 2)):
+        tok = O.oracle_forward(XH, wg_t, wu_t, WD, "int8", 2, k).tokens[0]
+        assert math.isclose(tok.t, hh[j], rel_tol=1e-14), (k, tok.t, hh[j])
+    assert math.isnan(O.oracle_forward(XH, wg_t, wu_t, WD, "int8", 2, 0).tokens[0].t)
+
+
+def test_p9_threshold_is_kth():
+    check_threshold_hand()
+
+
+def test_p9_threshold_random_is_smallest_kept():
+    # on tie-free data t equals the smallest |h~| among the kept channels
+    x, wg, wu, wd = _case(256, 200, 3, 41)
+    for k in (1, 57, 199, 200):
+        for tok in O.oracle_forward(x, wg, wu, wd, "int8", 180, k).tokens:
+            assert tok.t == float(np.min(np.abs(tok.h_hat[tok.mask])))
+
+
+# ---------------------------------------------------------------------------
+# P10. The mask acceptance band is relative to t: a differing channel is
+# excused when | |h~_j| - t | <= band * t.  Hand-built results at both edges
+# of the band, at a small and a large t (an absolute band would swap the
+# verdicts at both).
+# ---------------------------------------------------------------------------
+
+def _tok(h_hat, mask, t):
+    h = np.asarray(h_hat, dtype=np.float64)
+    return O.TokenResult(np.arange(0), h, h, h, np.abs(h).astype(np.float32),
+                         np.asarray(mask, dtype=np.int64), float(t), None, None)
+
+
+def check_band_edges():
+    band = 1e-6
+    for t in (1e-3, 1.0, 1e3):
+        inside, outside = t * (1 - 0.5 * band), t * (1 - 4 * band)
+        # oracle keeps {0, 1} (channel 1 is the k-th, at t); the GPU swapped 1 for 2
+        tok = _tok([5 * t, t, inside], [0, 1], t)
+        exc, unexc, diff = O.mask_diff(tok, np.array([0, 2]), band)
+        assert (exc, unexc, diff) == (2, 0, [1, 2]), (t, exc, unexc)
+        tok = _tok([5 * t, t, outside], [0, 1], t)
+        exc, unexc, diff = O.mask_diff(tok, np.array([0, 2]), band)
+        assert (exc, unexc) == (1, 1), (t, exc, unexc)
+        # a channel far from t is never excused
+        tok = _tok([5 * t, t, 0.5 * t], [0, 1], t)
+        assert O.mask_diff(tok, np.array([1, 2]), band)[1] == 2
+    # identical masks: nothing to excuse
+    assert O.mask_diff(_tok([1.0, 2.0], [1], 2.0), np.array([1]), band) == (0, 0, [])
+
+
+def test_p10_mask_band_relative():
+    check_band_edges()
+
+
+# ---------------------------------------------------------------------------
+# P11. The ranking key.  The pages fix no precision for the magnitude
+# ranking; both sides rank fp32(|h~|).  Ranking the float64 |h~| instead can
+# change the mask only among channels whose |h~| lies within fp32 rounding
+# (2^-24 relative) of t, i.e. well inside the acceptance band: brute force
+# of both rankings on random and tie-heavy data.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,data", [("int8", "small"), ("int4", "small"), ("int8", "ties")])
+def test_p11_fp32_key_vs_fp64_ranking(kind, data):
+    d = 256 if kind == "int4" else 96
+    x, wg, wu, wd = _case(d, 300, 4, 17, data)
+    for k in (1, 90, 299):
+        for tok in O.oracle_forward(x, wg, wu, wd, kind, d // 2, k).tokens:
+            a = np.abs(tok.h_hat)
+            order64 = np.lexsort((np.arange(a.size), -a))[:k]
+            diff = set(order64.tolist()) ^ set(tok.mask.tolist())
+            for j in diff:
+                assert abs(a[j] - tok.t) <= 2.0 ** -24 * tok.t, (j, a[j], tok.t)
+            assert np.array_equal(tok.key, a.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes in the parts P7-P10 pin.
+# ---------------------------------------------------------------------------
+
+def test_mutant_int4_scales_tiled(monkeypatch):
+    # scale of row i taken as s[i % G] instead of s[i // 128]
+    def bad(w, kind):
+        if kind != "int4":
+            return orig(w, kind)
+        q, s = O.quantize_int4_g128(w)
+        s_rows = np.tile(s.astype(np.float64), (w.shape[0] // s.shape[0], 1))
+        return O.Proxy(kind, q, s, q.astype(np.float64) * s_rows)
+    orig = O.build_proxy
+    monkeypatch.setattr(O, "build_proxy", bad)
+    assert _caught(lambda: check_int4_two_groups(0))
+
+
+def test_mutant_threshold_next_channel(monkeypatch):
+    # t taken at the first dropped channel instead of the k-th kept one
+    orig = O.stage1_token
+
+    def bad(x, pg, pu, k_in, k_ff):
+        s_in, g, u, h, key, mask, t = orig(x, pg, pu, k_in, k_ff)
+        order = np.lexsort((np.arange(key.shape[0]), -key))
+        if k_ff < key.shape[0]:
+            t = float(abs(h[order[k_ff]]))
+        return s_in, g, u, h, key, mask, t
+    monkeypatch.setattr(O, "stage1_token", bad)
+    assert _caught(check_threshold_hand)
+
+
+def test_mutant_band_absolute(monkeypatch):
+    def bad(tok, gpu_mask, band=1e-6):
+        a, b = set(np.asarray(tok.mask).tolist()), set(np.asarray(gpu_mask).tolist())
+        diff = sorted(a ^ b)
+        exc = sum(1 for j in diff if abs(abs(tok.h_hat[j]) - tok.t) <= band)
+        return exc, len(diff) - exc, diff
+    monkeypatch.setattr(O, "mask_diff", bad)
+    assert _caught(check_band_edges)
+
+
+def test_mutant_bf16_shift(monkeypatch):
+    def bad(bits):
+        b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+        return b.view(np.float32).astype(np.float64)
+    monkeypatch.setattr(O, "bf16_bits_to_f64", bad)
+    assert _caught(test_p7_bf16_bits_hand_values)
