@@ -23,8 +23,7 @@ from typing import Dict, Optional, Tuple
 import torch  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# PROX_HIP_LIB selects another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("PROX_HIP_LIB") or os.path.join(_HERE, "libprox_hip.so")
+LIB_PATH = os.path.join(_HERE, "libprox_hip.so")
 
 PROX_OK = 0
 KINDS = {"int8": 1, "int4": 2}
@@ -52,7 +51,7 @@ class _Proxy(ctypes.Structure):
 class _Taps(ctypes.Structure):
     _fields_ = [("in_idx", ctypes.c_void_p), ("key", ctypes.c_void_p), ("h_hat", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("stream_idx", ctypes.c_void_p)]
 
 
 N_PHASES = 3
@@ -97,6 +96,13 @@ def _check(st: int, where: str) -> None:
 
 def abi_version() -> int:
     return _lib.prox_abi_version()
+
+
+def library_sha256() -> str:
+    """sha256 (first 16 hex digits) of the loaded library file."""
+    import hashlib
+    with open(LIB_PATH, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
 def proxy_bytes(d_model: int, d_ff: int, kind: str) -> int:
@@ -206,7 +212,7 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     sp = _stream_ptr(stream)
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*[getattr(e, "cuda_event", e) for e in events])
-        ct = _Taps(None, None, None, arr, len(events), 0)
+        ct = _Taps(None, None, None, arr, len(events), 0, None)
         _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
                                           ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),
                                           mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
@@ -216,14 +222,17 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     if taps:
         t = {"in_idx": torch.empty(B, max(k_in, 1), dtype=torch.int32, device=dev),
              "key": torch.empty(B, F, dtype=torch.float32, device=dev),
-             "h_hat": torch.empty(B, F, dtype=torch.float64, device=dev)}
-        ct = _Taps(t["in_idx"].data_ptr(), t["key"].data_ptr(), t["h_hat"].data_ptr(), None, 0, 0)
+             "h_hat": torch.empty(B, F, dtype=torch.float64, device=dev),
+             "stream_idx": torch.full((B, max(k_ff, 1)), -1, dtype=torch.int32, device=dev)}
+        ct = _Taps(t["in_idx"].data_ptr(), t["key"].data_ptr(), t["h_hat"].data_ptr(), None, 0, 0,
+                   t["stream_idx"].data_ptr())
         _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
                                           ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),
                                           mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
                                           workspace.numel(), ctypes.byref(ct), sp),
                "prox_ffn_forward_taps")
         t["in_idx"] = t["in_idx"][:, :k_in]
+        t["stream_idx"] = t["stream_idx"][:, :k_ff]
         return y, mask, idx[:, :k_ff], t
     _check(_lib.prox_ffn_forward(x.data_ptr(), B, ctypes.byref(weights._c), ctypes.byref(proxy.desc),
                                  k_in, k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(),
@@ -232,5 +241,5 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     return y, mask, idx[:, :k_ff]
 
 
-__all__ = ["Weights", "Proxy", "ProxError", "abi_version", "proxy_bytes", "workspace_bytes",
+__all__ = ["Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
            "build_proxy", "alloc_workspace", "ffn_forward", "LIB_PATH", "KINDS", "N_PHASES", "PHASES"]

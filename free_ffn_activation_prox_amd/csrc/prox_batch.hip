@@ -11,8 +11,12 @@
 //                 0 elsewhere
 //   proxy GEMM    g~ = X~ W~_gate, u~ = X~ W~_up over the quantized proxy.
 //                 Codes are small integers and x is bf16, so every product is
-//                 exact in fp32; the unit accumulates 32 of them, and those
-//                 sums are added in fp64 (int4: times the group scale first).
+//                 exact in fp32.  Four MFMAs (128 rows, one int4 group) chain
+//                 in the fp32 accumulator, then the sum moves to fp64 (int4:
+//                 times the group scale).  That fp32 sum of 128 exact
+//                 products is not exact: its error is at most 127 * 2^-24 of
+//                 the sum of the products' magnitudes (recursive summation;
+//                 fewer roundings if the unit adds its 32 products at once).
 //                 key = fp32(|silu(g~) u~|) with h~ formed in fp64.
 //   selection     the per-token top-k_ff over the keys (the same kernel as the
 //                 single-token path, selection only)
@@ -357,19 +361,7 @@ __global__ void __launch_bounds__(KIND == 1 ? 256 : 512) k_proxy_batch(PbArgs a)
             }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
         __syncthreads();
-        if (t == 0) {
-            unsigned long long* cnt = a.tcnt + tile;
-            unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (;;) {
-                const unsigned long long nxt =
-                    (cur >> 32) == a.gen ? cur + 1 : (((unsigned long long)a.gen << 32) | 1ull);
-                if (__hip_atomic_compare_exchange_strong(cnt, &cur, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT)) {
-                    flag = (int)(nxt & 0xffffffffull) == a.ks1 ? 1 : 0;
-                    break;
-                }
-            }
-        }
+        if (t == 0) flag = tile_arrive(a.tcnt + tile, a.gen, a.ks1);
         __syncthreads();
         if (!flag) return;
 #pragma unroll
@@ -743,7 +735,12 @@ __global__ void __launch_bounds__(256) k_down_batch(DnArgs a) {
     for (int s0 = 0; s0 < nst; s0 += PD) {
 #pragma unroll
         for (int i = 0; i < PD; ++i) {
-            uint16_t* buf = lds + (i & 1) * TILE;
+            // alternate buffers by the global stage index: with an odd PD,
+            // (i & 1) would give the last stage of a round and the first of
+            // the next the same buffer, and a wave could overwrite it while
+            // another still reads it (one barrier per stage only orders
+            // stages that use different buffers)
+            uint16_t* buf = lds + ((s0 + i) & 1) * TILE;
             store_stage(ring[i], buf);
             lds_barrier();
             mma_stage(ring[i], buf);

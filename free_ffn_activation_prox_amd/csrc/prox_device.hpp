@@ -37,6 +37,26 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Arrival at a split tile: the counter holds (call tag << 32 | arrivals).  The
+// arrival that completes the tile stores 0 back, so every call leaves its
+// counters clear (a replayed graph reuses one tag); a counter holding anything
+// else with another tag (a workspace never cleared, an interrupted call)
+// restarts at 1.  Returns 1 for the arrival that completes the tile.
+__device__ __forceinline__ int tile_arrive(unsigned long long* cnt, uint32_t gen, int nseg) {
+    unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const bool same = (cur >> 32) == gen || cur == 0ull;
+        const unsigned long long nxt = same ? ((((unsigned long long)gen << 32) | (cur & 0xffffffffull)) + 1ull)
+                                            : (((unsigned long long)gen << 32) | 1ull);
+        if (__hip_atomic_compare_exchange_strong(cnt, &cur, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+            if ((int)(nxt & 0xffffffffull) != nseg) return 0;
+            __hip_atomic_store(cnt, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return 1;
+        }
+    }
+}
+
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -98,14 +118,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     return xor32_add(v);
 }
 
-// Inclusive prefix sum over the wave (row_shr 1, 2, 4, 8, then row broadcasts).
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+// Inclusive prefix sum over the wave (row_shr 1, 2, 4, 8, then row broadcasts),
+// modulo 2^32 (callers pack two 16-bit counts into one word).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
     return x;
 }
 
@@ -125,25 +146,35 @@ __device__ __forceinline__ int wave_max(int v) {
     return v;
 }
 
-// Exclusive prefix sum over the block in thread order; `total` = block sum.
-// `lds` holds >= 16 ints.  Every thread of the block must call it.
+// Exclusive prefix sum over the block in thread order, modulo 2^32; `total` =
+// block sum.  `lds` holds >= 16 words.  Every thread of the block must call it.
 template <int NT>
-__device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, int* lds, uint32_t& total) {
     constexpr int NW = NT / kWave;
     const int lane = lane_id(), w = threadIdx.x / kWave;
-    const int incl = wave_incl_scan(v);
-    if (lane == kWave - 1) lds[w] = incl;
+    const uint32_t incl = wave_incl_scan(v);
+    uint32_t* l32 = reinterpret_cast<uint32_t*>(lds);
+    if (lane == kWave - 1) l32[w] = incl;
     lds_barrier();
-    int off = 0, tot = 0;
+    uint32_t off = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        const int c = lds[i];
+        const uint32_t c = l32[i];
         tot += c;
-        off += i < w ? c : 0;
+        off += i < w ? c : 0u;
     }
     lds_barrier();
     total = tot;
     return off + incl - v;
+}
+
+// The same for non-negative counts whose block total stays below 2^31.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* lds, int& total) {
+    uint32_t tot;
+    const uint32_t r = block_excl_scan_u32<NT>((uint32_t)v, lds, tot);
+    total = (int)tot;
+    return (int)r;
 }
 
 template <int NT>

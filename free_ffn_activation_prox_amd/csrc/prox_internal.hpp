@@ -131,7 +131,8 @@ hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyV
                          hipStream_t s);
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
                          const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
-                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, hipStream_t s);
+                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, int32_t* stream_tap,
+                         hipStream_t s);
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s);
 // Stage-2 selection only: mask (required) and idx (nullable) from the keys.
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,

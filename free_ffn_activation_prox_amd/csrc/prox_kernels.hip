@@ -1,17 +1,18 @@
-// Prox sparse SwiGLU FFN: gfx950 kernels.
+// Prox sparse SwiGLU FFN: gfx950 kernels of the single-token path (fewer than
+// 4 tokens per call) and the one-time proxy build.
 //
-// One forward = four launches (Prox, Abstract; SwiGLU as in PrunePath, §2.1, Eq. (1)):
-//   stage1   per (block, token): input selection (top-k_in of |x|, redone in
-//            every block: x is a few KB), then the block's equal share of the
-//            (channel tile, kept-row chunk) items of the proxy GEMV
-//   score    per (channel tile, token): the tile's partial sums in a fixed
-//            order, h~ = silu(g~) u~ in fp64 and the fp32 ranking key |h~|
-//   stage2   per (block, token): top-k of the keys (threshold bin from a
-//            coarse LDS histogram, redone in every block), the block's share of the kept
-//            channels, then for each of them the exact gate/up dots over the
-//            dense x, h = silu(g) u and h * W_down row into the block's partial y
-//   reduce   y = fixed-order sum of the block partials
-// plus the one-time proxy build.
+// One forward = three launches (Prox, Abstract; SwiGLU as in PrunePath, §2.1, Eq. (1)):
+//   k_stage1  per (block, token): input selection (top-k_in of |x|, redone in
+//             every block: x is a few KB), the block's share of the (channel
+//             tile, kept-row chunk) items of the proxy GEMV, and for every
+//             tile the block completes: h~ = silu(g~) u~ in fp64 and the fp32
+//             ranking key |h~|
+//   k_stage2  per (block, token): top-k of the keys (threshold bin from a
+//             coarse LDS histogram, redone in every block), the block's share
+//             of the kept channels, then for each of them the exact gate/up
+//             dots over the dense x, h = silu(g) u and h * W_down row into the
+//             block's partial y
+//   k_reduce_y  y = fixed-order sum of the block partials
 //
 // Proxy layout (tile-major): the codes of one channel tile (64 channels int8,
 // 128 channels int4) for input row i are one 128-byte line at
@@ -176,18 +177,6 @@ __device__ __host__ __forceinline__ int s1_block_of(long long i, long long T, in
     return (int)(((i + 1) * nb1 - 1) / T);
 }
 
-// Arrival at a split tile: the counter holds (call tag << 32 | arrivals); a
-// counter left by an earlier call (or never cleared) carries another tag and
-// restarts at 1.  Returns 1 for the arrival that completes the tile.
-__device__ __forceinline__ int s1_arrive(unsigned long long* cnt, uint32_t gen, int nseg) {
-    unsigned long long cur = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        const unsigned long long nxt = (cur >> 32) == gen ? cur + 1 : (((unsigned long long)gen << 32) | 1ull);
-        if (__hip_atomic_compare_exchange_strong(cnt, &cur, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            return (int)(nxt & 0xffffffffull) == nseg ? 1 : 0;
-    }
-}
 
 // h~ = silu(g~) u~ in fp64 (int8: per-channel scales applied here) and the
 // fp32 ranking key |h~|.
@@ -320,9 +309,9 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         gt += key[q] > T ? 1 : 0;
         eq += (key[q] == T && !all) ? 1 : 0;
     }
-    int tot;
+    uint32_t tot;
     // fewer than k_in <= 2^15 keys exceed T (keep-all: at most d keys, unpacked)
-    const uint32_t pre = (uint32_t)block_excl_scan<NT>(all ? gt : (int)(((uint32_t)gt << 16) | (uint32_t)eq), sc, tot);
+    const uint32_t pre = block_excl_scan_u32<NT>(all ? (uint32_t)gt : (((uint32_t)gt << 16) | (uint32_t)eq), sc, tot);
     // Which keys are kept, and the list order.  The kept inputs whose
     // exponent is at most 5 above the threshold's ("band B") come first, the
     // larger ones after, each part in index order: chunks of band B span at
@@ -349,8 +338,8 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         nb += on[q] && !big ? 1 : 0;
         na += on[q] && big ? 1 : 0;
     }
-    int tot2;
-    const uint32_t pre2 = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)nb << 16) | (uint32_t)na), sc, tot2);
+    uint32_t tot2;
+    const uint32_t pre2 = block_excl_scan_u32<NT>(((uint32_t)nb << 16) | (uint32_t)na, sc, tot2);
     if (k_in > 0) {
         int pb = (int)(pre2 >> 16), pa = (int)((uint32_t)tot2 >> 16) + (int)(pre2 & 0xffffu);
         uint32_t* dummy = list + k_in + lane;              // lanes with nothing to write
@@ -652,7 +641,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
             __syncthreads();
-            if (t == 0) sc[22] = s1_arrive(a.tcnt + (size_t)b * a.tiles + tile, a.gen, w1 - w0 + 1);
+            if (t == 0) sc[22] = tile_arrive(a.tcnt + (size_t)b * a.tiles + tile, a.gen, w1 - w0 + 1);
             lds_barrier();
             last = sc[22] != 0;
             if (last && t < 2 * TC) {
@@ -722,6 +711,7 @@ struct Stage2Args {
     int32_t* idx;         // [B][k] or null
     uint8_t* mask;        // [B][F] or null
     float* ypart;         // [B][W2][d]
+    int32_t* stream_tap;  // [B][k] or null: the channels the blocks stream, by share
 };
 
 constexpr int kS2Threads = 512;
@@ -961,8 +951,9 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         cdm |= is_cand(kb[q]) ? (1ull << q) : 0ull;
     }
     const int ncert_t = __popcll(cem), nd = __popcll(cdm);
-    int tot;
-    const uint32_t pre = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)ncert_t << 16) | (uint32_t)nd), sc, tot);
+    // both counts fit 16 bits (F <= 32768); the packed total may reach 2^31
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan_u32<NT>(((uint32_t)ncert_t << 16) | (uint32_t)nd, sc, tot);
     const int ncand = (int)((uint32_t)tot & 0xffffu);
     const int C = (int)((uint32_t)tot >> 16);            // certain keys in all
     const int crank0 = (int)(pre >> 16), cp0 = (int)(pre & 0xffffu);
@@ -1006,7 +997,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     RowGroup<R, G> cur, nxt;
     if constexpr (STREAM) load_group<R, G>(rs, chan, 0, E, row_bytes, mat_bytes, voff, cur);
 
-    int nks = 0, kc_before = 0;
+    int nks = 0, kc_before = 0, s0k = 0;
     if (listed) {
         // ---- resolve the candidates while those loads are in flight:
         // cidx[i] gets bit 15 when kept
@@ -1072,6 +1063,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         const int KC = run;
         const int s0 = (int)((long long)w * KC / W2), s1 = (int)((long long)(w + 1) * KC / W2);
         nks = s1 - s0;
+        s0k = s0;
         for (int i = t; i < ncand; i += NT) {
             const int r = kr[i];
             if (STREAM && (cidx[i] & 0x8000u) && r >= s0 && r < s1) chan[nc + r - s0] = cidx[i] & 0x7fffu;
@@ -1092,8 +1084,8 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             gt += (int)kb[q] >= 0 && kb[q] > T ? 1 : 0;
             eq += kb[q] == T ? 1 : 0;
         }
-        int tk;
-        const uint32_t pk = (uint32_t)block_excl_scan<NT>((int)(((uint32_t)gt << 16) | (uint32_t)eq), sc, tk);
+        uint32_t tk;
+        const uint32_t pk = block_excl_scan_u32<NT>(((uint32_t)gt << 16) | (uint32_t)eq, sc, tk);
         int eb = (int)(pk & 0xffffu);
         int pos = (int)(pk >> 16) + min(eb, need);
         const int k0 = (int)((long long)w * k / W2), k1 = (int)((long long)(w + 1) * k / W2);
@@ -1142,6 +1134,14 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     if constexpr (!STREAM) {         // selection only: mask and idx are written
         write_range();
         return;
+    }
+    if (a.stream_tap) {
+        // the streamed list, at the ranks of the block's shares: certain keys
+        // [c0, c1), then kept candidates at C + [s0, s1) (slow path: kept ranks
+        // [k0, k1)); over all blocks, a permutation of the token's idx
+        const int base1 = listed ? c0 : (int)((long long)w * k / W2);
+        for (int i = t; i < n; i += NT)
+            a.stream_tap[(size_t)b * k + (i < nc ? base1 + i : C + s0k + (i - nc))] = chan[i];
     }
 
     // ---- sparse SwiGLU: group 0 = entries [0, E), then [E, n) G at a time.
@@ -1227,8 +1227,9 @@ static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
 
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
                          const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
-                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, hipStream_t s) {
-    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart};
+                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, int32_t* stream_tap,
+                         hipStream_t s) {
+    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart, stream_tap};
     // channels per group: the fewest that keep the stream at its rate (more
     // rows in flight per block measured slower on the 4096 and 8192 shapes)
     if (d <= 4096) return stage2_pk<1, 2, true>(a, B, s);
@@ -1238,7 +1239,7 @@ hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t
 
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
                          int32_t* idx, uint8_t* mask, hipStream_t s) {
-    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr};
+    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr, nullptr};
     return stage2_pk<1, 1, false>(a, B, s);
 }
 

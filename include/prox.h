@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PROX_ABI_VERSION 1
+#define PROX_ABI_VERSION 2
 
 typedef enum {
     PROX_OK = 0,
@@ -119,7 +119,11 @@ typedef struct {
  * the stream before the first launch and events[p + 1] after phase p.  A phase
  * is one kernel below 4 tokens per call; from 4 tokens stage 1 is the input
  * selection and the proxy GEMM, stage 2 the channel selection, gate/up and
- * down projections.                                                          */
+ * down projections.
+ *   stream_idx [batch][k_ff]  below 4 tokens per call only (untouched from 4):
+ *          the channels whose rows the Stage-2 blocks actually stream, each
+ *          block's list at the ranks of its share; over all blocks a
+ *          permutation of idx when no channel is lost or streamed twice.     */
 typedef struct {
     int32_t* in_idx;
     float* key;
@@ -127,6 +131,7 @@ typedef struct {
     void* const* events;
     int32_t n_events;
     int32_t reserved;
+    int32_t* stream_idx;
 } prox_taps;
 
 /* ABI version compiled into the library (PROX_ABI_VERSION). */

@@ -124,8 +124,10 @@ def build_proxy(w: np.ndarray, kind: str) -> Proxy:
         wt = q.astype(np.float64) * s.astype(np.float64)[None, :]
     elif kind == "int4":
         q, s = quantize_int4_g128(w)
-        s_rows = np.repeat(s.astype(np.float64), INT4_GROUP, axis=0)
-        wt = q.astype(np.float64) * s_rows
+        d, F = q.shape
+        # W~[i, j] = s[i // 128, j] * q[i, j]: rows of group g take scale row g
+        wt = (q.astype(np.float64).reshape(d // INT4_GROUP, INT4_GROUP, F)
+              * s.astype(np.float64)[:, None, :]).reshape(d, F)
     elif kind == "exact":
         q, s, wt = None, None, np.asarray(w, dtype=np.float64)
     else:
@@ -178,46 +180,82 @@ class ForwardResult:
         return [t.mask for t in self.tokens]
 
 
-def stage1_token(x: np.ndarray, pg: Proxy, pu: Proxy, k_in: int, k_ff: int):
-    """Stage 1 for one token (Prox, Abstract): input sparsity, proxy
-    pre-activations, approximate intermediate, magnitude ranking, mask."""
-    x = np.asarray(x, dtype=np.float64)
+def keep_mask(x: np.ndarray, k_in: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Input sparsity for one token: S_in (ascending) and x with every input
+    outside S_in set to zero."""
     s_in = select_topk(np.abs(x), k_in)
-    xs = x[s_in]
-    g_hat = xs @ pg.w_tilde[s_in, :]
-    u_hat = xs @ pu.w_tilde[s_in, :]
+    xk = np.zeros_like(x)
+    xk[s_in] = x[s_in]
+    return s_in, xk
+
+
+def stage1_batch(x: np.ndarray, pg: Proxy, pu: Proxy, k_in: int, k_ff: int):
+    """Stage 1 for tokens x [B][d] (Prox, Abstract): input sparsity, proxy
+    pre-activations, approximate intermediate, magnitude ranking, mask.
+
+    g~_j = sum over i in S_in of x_i W~_gate[i, j] is evaluated as one matrix
+    product of x with its dropped inputs set to zero (each dropped term is an
+    exact zero), one row per token.  Returns one tuple per token:
+    (s_in, g~, u~, h~, key, mask, t)."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    kept = [keep_mask(x[b], k_in) for b in range(x.shape[0])]
+    xk = np.stack([k[1] for k in kept])
+    g_hat = xk @ pg.w_tilde
+    u_hat = xk @ pu.w_tilde
     h_hat = silu(g_hat) * u_hat
-    key = np.abs(h_hat).astype(np.float32)
-    mask = select_topk(key, k_ff)
-    if k_ff > 0:
-        kth = np.lexsort((np.arange(key.shape[0]), -key))[k_ff - 1]
-        t = float(abs(h_hat[kth]))
-    else:
-        t = float("nan")
-    return s_in, g_hat, u_hat, h_hat, key, mask, t
+    out = []
+    for b in range(x.shape[0]):
+        key = np.abs(h_hat[b]).astype(np.float32)
+        mask = select_topk(key, k_ff)
+        if k_ff > 0:
+            kth = np.lexsort((np.arange(key.shape[0]), -key))[k_ff - 1]
+            t = float(abs(h_hat[b, kth]))
+        else:
+            t = float("nan")
+        out.append((kept[b][0], g_hat[b], u_hat[b], h_hat[b], key, mask, t))
+    return out
+
+
+def stage1_token(x: np.ndarray, pg: Proxy, pu: Proxy, k_in: int, k_ff: int):
+    """Stage 1 for one token x [d]; see stage1_batch."""
+    return stage1_batch(np.asarray(x, dtype=np.float64)[None, :], pg, pu, k_in, k_ff)[0]
+
+
+def stage2_batch(x: np.ndarray, wg_t: np.ndarray, wu_t: np.ndarray, wd: np.ndarray,
+                 masks) -> Tuple[List[np.ndarray], np.ndarray]:
+    """Stage 2 for tokens x [B][d] with per-token masks (Prox, Abstract: the
+    selected channels computed exactly; COUNTDOWN, Abstract: y is a
+    combination of W_down rows).
+
+    g_j = sum_i x_i W_gate[i, j] over the dense x, h_j = silu(g_j) u_j for j in
+    the token's mask, y = sum over the mask of h_j W_down[j, :], evaluated as
+    matrix products with h set to zero outside the mask (exact zeros).
+    Returns (h on each mask, in mask order; y [B][d])."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    B = x.shape[0]
+    g = x @ wg_t.T
+    u = x @ wu_t.T
+    h_all = silu(g) * u
+    hm = np.zeros_like(h_all)
+    hs = []
+    for b in range(B):
+        m = np.asarray(masks[b], dtype=np.int64)
+        hm[b, m] = h_all[b, m]
+        hs.append(h_all[b, m])
+    return hs, hm @ wd
 
 
 def stage2_token(x: np.ndarray, wg_t: np.ndarray, wu_t: np.ndarray, wd: np.ndarray,
                  mask: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Stage 2 for one token (Prox, Abstract: selected channels computed
-    exactly; COUNTDOWN, Abstract: y is a combination of W_down rows).
-
-    g_j = sum_i x_i W_gate[i, j] over the dense x, h_j = silu(g_j) u_j,
-    y = sum_{j in mask} h_j W_down[j, :]."""
-    x = np.asarray(x, dtype=np.float64)
-    m = np.asarray(mask, dtype=np.int64)
-    g = wg_t[m, :] @ x
-    u = wu_t[m, :] @ x
-    h = silu(g) * u
-    y = h @ wd[m, :] if m.size else np.zeros(wd.shape[1], dtype=np.float64)
-    return h, y
+    """Stage 2 for one token x [d]; see stage2_batch.  Returns (h [k], y [d])."""
+    hs, y = stage2_batch(np.asarray(x, dtype=np.float64)[None, :], wg_t, wu_t, wd, [mask])
+    return hs[0], y[0]
 
 
 def oracle_stage2(x: np.ndarray, wg_t: np.ndarray, wu_t: np.ndarray, wd: np.ndarray,
                   masks) -> np.ndarray:
     """Stage 2 for a batch with caller-given per-token masks -> y [B][d]."""
-    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
-    return np.stack([stage2_token(x[b], wg_t, wu_t, wd, masks[b])[1] for b in range(x.shape[0])])
+    return stage2_batch(x, wg_t, wu_t, wd, masks)[1]
 
 
 def oracle_forward(x: np.ndarray, wg_t: np.ndarray, wu_t: np.ndarray, wd: np.ndarray,
@@ -238,11 +276,11 @@ def oracle_forward(x: np.ndarray, wg_t: np.ndarray, wu_t: np.ndarray, wd: np.nda
     if proxies is None:
         proxies = (build_proxy(wg_t.T, kind), build_proxy(wu_t.T, kind))
     pg, pu = proxies
+    s1 = stage1_batch(x, pg, pu, k_in, k_ff)
+    hs, y = stage2_batch(x, wg_t, wu_t, wd, [r[5] for r in s1])
     res = ForwardResult()
-    for b in range(x.shape[0]):
-        s_in, g_hat, u_hat, h_hat, key, mask, t = stage1_token(x[b], pg, pu, k_in, k_ff)
-        h, y = stage2_token(x[b], wg_t, wu_t, wd, mask)
-        res.tokens.append(TokenResult(s_in, g_hat, u_hat, h_hat, key, mask, t, h, y))
+    for b, (s_in, g_hat, u_hat, h_hat, key, mask, t) in enumerate(s1):
+        res.tokens.append(TokenResult(s_in, g_hat, u_hat, h_hat, key, mask, t, hs[b], y[b]))
     return res
 
 

@@ -19,7 +19,8 @@ Activations x are Laplace(0, 1) in fp32; c1/c2 scale 4 fixed outlier dims by
 20, c4 scales round(0.5 % of d) = 41 outlier dims by 30, c3/c5 divide each
 token by its RMS.  Everything is rounded to bf16 at the end.
 
-Random streams are numpy ``default_rng([seed, config, layer, tensor])`` so any
+Random streams are numpy ``default_rng([seed, config, layer, tensor])`` (weight
+matrices: one stream per chunk of 1024 rows, ``[..., tensor, chunk]``) so any
 tensor can be regenerated on its own.  Layout: ``wg_t`` and ``wu_t`` are
 [F][d] (row j = intermediate channel j, i.e. the gate/up weight of a
 bias-free linear layer stored output-major); ``wd`` is [F][d] as in the
@@ -28,6 +29,8 @@ SwiGLU definition, where row j of W_down is the output direction of channel j.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Tuple
 
@@ -87,6 +90,10 @@ class Workload:
     def k_ff(self, layer: int = 0) -> int:
         return pct_count(self.layers[layer].F, 100 - self.sparsity_pct)
 
+    @property
+    def n_layers(self) -> int:
+        return len(self.layers)
+
 
 def _stack(shapes: List[LayerShape], n: int) -> Tuple[LayerShape, ...]:
     return tuple(shapes[i % len(shapes)] for i in range(n))
@@ -113,20 +120,44 @@ def workloads() -> Dict[str, Workload]:
     return w
 
 
-def _rng(config_id: int, layer: int, tensor: int, seed: int = ROOT_SEED) -> np.random.Generator:
-    return np.random.default_rng([seed, config_id, layer, tensor])
+def _rng(config_id: int, layer: int, tensor: int, seed: int = ROOT_SEED, *more: int) -> np.random.Generator:
+    return np.random.default_rng([seed, config_id, layer, tensor, *more])
+
+
+_CHUNK_ROWS = 1024          # rows of a weight matrix drawn from one stream
+_THREADS = min(8, os.cpu_count() or 1)
+
+
+def _normal_bf16(config_id: int, layer: int, tensor: int, rows: int, cols: int, std: float,
+                 seed: int) -> np.ndarray:
+    """N(0, std) fp32 -> bf16 bits [rows][cols]; rows drawn in chunks of
+    _CHUNK_ROWS, chunk c from stream (seed, config, layer, tensor, c), so the
+    chunks can be filled by several threads and the result does not depend on
+    how many."""
+    out = np.empty((rows, cols), dtype=np.uint16)
+
+    def fill(c):
+        r0, r1 = c * _CHUNK_ROWS, min(rows, (c + 1) * _CHUNK_ROWS)
+        a = np.empty((r1 - r0, cols), dtype=np.float32)
+        _rng(config_id, layer, tensor, seed, c).standard_normal(out=a, dtype=np.float32)
+        a *= np.float32(std)
+        out[r0:r1] = bf16_round(a)
+
+    n = (rows + _CHUNK_ROWS - 1) // _CHUNK_ROWS
+    if n <= 1:
+        for c in range(n):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(max_workers=_THREADS) as ex:
+            list(ex.map(fill, range(n)))
+    return out
 
 
 def gen_weights(config_id: int, layer: int, d: int, F: int, std: float = 0.02,
                 seed: int = ROOT_SEED) -> Dict[str, np.ndarray]:
     """bf16 bit patterns: wg_t, wu_t [F][d] and wd [F][d]."""
-    out = {}
-    for name, tid in (("wg_t", _T_GATE), ("wu_t", _T_UP), ("wd", _T_DOWN)):
-        r = _rng(config_id, layer, tid, seed)
-        a = r.standard_normal((F, d), dtype=np.float32)
-        a *= np.float32(std)
-        out[name] = bf16_round(a)
-    return out
+    return {name: _normal_bf16(config_id, layer, tid, F, d, std, seed)
+            for name, tid in (("wg_t", _T_GATE), ("wu_t", _T_UP), ("wd", _T_DOWN))}
 
 
 def outlier_dims(config_id: int, d: int, count: int, seed: int = ROOT_SEED) -> np.ndarray:

@@ -6,9 +6,19 @@ Acceptance per token (the bar the path is held to):
   * kept-input lists identical;
   * channel masks identical except channels whose oracle score lies within
     1e-6 (relative) of the k-th score t ("excused");
-  * max |y_gpu - y_ref| <= 2e-2 * max |y_ref|, where y_ref is the oracle's
-    Stage 2 on the GPU's own mask (identical to the oracle's y when the masks
-    agree).
+  * max |y_gpu - y_ref| <= 2e-2 * max |y_ref| (the contract), where y_ref is
+    the oracle's Stage 2 on the GPU's own mask (identical to the oracle's y
+    when the masks agree); and a second bar of 1e-4 * max |y_ref|, the fp32
+    accumulation bound below, which a lost or doubled channel exceeds;
+  * below 4 tokens per call: the channels the Stage-2 blocks stream are a
+    permutation of idx (no channel lost, none streamed twice).
+
+The second y bar: y is a sum of at most F fp32 products h_j W_down[j, c],
+accumulated in fp32 (per block, then a fixed-order sum of the block
+partials); h_j itself carries the fp32 error of a d-term dot product (the
+matrix-core path adds the rounding of h to 16 significant bits, as two bf16
+halves).  Measured errors are below 5e-6 of max |y|; 1e-4 leaves a factor
+of 20 while one channel near the threshold moves y by about 1e-2 of max |y|.
 """
 
 from __future__ import annotations
@@ -20,6 +30,7 @@ import free_ffn_activation_prox_amd as P
 from oracle import prox_oracle as O
 
 Y_TOL = 2e-2
+Y_TIGHT = 1e-4
 BAND = 1e-6
 
 
@@ -95,28 +106,36 @@ class Case:
         in_idx = taps["in_idx"].cpu().numpy()
         key = taps["key"].cpu().numpy()
         hh = taps["h_hat"].cpu().numpy()
-        toks = range(self.B) if tokens is None else tokens
+        sidx = taps["stream_idx"].cpu().numpy()
+        toks = list(range(self.B)) if tokens is None else list(tokens)
         pg, pu = self.oracle_proxies()
         stats = {"excused": 0, "unexcused": 0, "key_bits_differ": 0, "max_rel_y": 0.0,
                  "max_rel_h": 0.0}
-        for b in toks:
-            s_in, g_hat, u_hat, h_hat, okey, omask, t = O.stage1_token(self.x[b], pg, pu, k_in, k_ff)
+        s1 = O.stage1_batch(self.x[toks], pg, pu, k_in, k_ff)
+        gms = [np.flatnonzero(mask[b]) for b in toks]
+        _, yrefs = O.stage2_batch(self.x[toks], self.wg, self.wu, self.wd, gms)
+        for n, b in enumerate(toks):
+            s_in, g_hat, u_hat, h_hat, okey, omask, t = s1[n]
             assert np.array_equal(in_idx[b], s_in), f"{label} token {b}: kept inputs differ"
             sc = max(np.max(np.abs(h_hat)), 1e-300)
             stats["max_rel_h"] = max(stats["max_rel_h"], float(np.max(np.abs(hh[b] - h_hat)) / sc))
             stats["key_bits_differ"] += int(np.sum(key[b].view(np.uint32) != okey.view(np.uint32)))
-            gm = np.flatnonzero(mask[b])
+            gm = gms[n]
             assert gm.size == k_ff, f"{label} token {b}: mask has {gm.size} channels, want {k_ff}"
             assert np.array_equal(idx[b], gm), f"{label} token {b}: idx is not the ascending mask"
+            if self.B < 4:
+                assert np.array_equal(np.sort(sidx[b]), gm), \
+                    f"{label} token {b}: the streamed channels are not the kept ones"
             tok = O.TokenResult(s_in, g_hat, u_hat, h_hat, okey, omask, t, None, None)
             exc, unexc, diff = O.mask_diff(tok, gm, BAND)
             stats["excused"] += exc
             stats["unexcused"] += unexc
             assert unexc == 0, f"{label} token {b}: {unexc} unexcused mask differences {diff[:8]}"
-            _, yref = O.stage2_token(self.x[b], self.wg, self.wu, self.wd, gm)
+            yref = yrefs[n]
             scale = np.max(np.abs(yref))
             err = np.max(np.abs(y[b] - yref))
             rel = float(err / scale) if scale > 0 else float(err)
             stats["max_rel_y"] = max(stats["max_rel_y"], rel)
             assert rel <= Y_TOL, f"{label} token {b}: y error {rel:.3e} > {Y_TOL}"
+            assert rel <= Y_TIGHT, f"{label} token {b}: y error {rel:.3e} > {Y_TIGHT} (accumulation bound)"
         return stats

@@ -161,3 +161,25 @@ def test_batch_many_equal_keys():
         for b in range(B):
             omask = O.stage1_token(c.x[b], pg, pu, k_in, k_ff)[5]
             assert np.array_equal(np.flatnonzero(mask[b].cpu().numpy()), np.asarray(omask)), (sp, b)
+
+
+@pytest.mark.parametrize("kind", ["int8", "int4"])
+@pytest.mark.parametrize("B", [24, 32])
+def test_batch_two_token_groups_long_slices(kind, B):
+    # 17..32 tokens (two token groups): the down projection keeps three stages
+    # in flight, and with d = 256, F = 8192 each channel slice holds 7-8
+    # stages, so its LDS buffers cross several round boundaries; y to the
+    # tight bar and bit for bit across two calls
+    import free_ffn_activation_prox_amd as P
+    d, F = 256, 8192
+    print(f"[batch] case {kind} d={d} F={F} B={B}", flush=True)
+    c = _case(d, F, B, seed=40 + B, kind=kind)
+    for keep, sp in ((60, 70), (100, 50)):
+        k_in, k_ff = pct_count(d, keep), pct_count(F, 100 - sp)
+        label = f"{kind} d={d} F={F} B={B} keep={keep} sp={sp}"
+        _report(label, c.check(k_in, k_ff, label=label))
+        a = P.ffn_forward(c.dx, c.weights, c.proxy, k_in, k_ff)
+        b = P.ffn_forward(c.dx, c.weights, c.proxy, k_in, k_ff)
+        for u, v in zip(a, b):
+            assert torch.equal(u, v), label
+

@@ -72,12 +72,18 @@ def test_c4_70b_batch8(name):
     _permuted(c, wl, 0)
 
 
-@pytest.mark.parametrize("layer", [0, 1])
-@pytest.mark.parametrize("name", ["c3_b1", "c3_b4", "c3_b16"])
+def test_c3_llama3_8b_stack_every_layer_batch1():
+    # all 32 layers of the stack, one token each: proxy bytes, kept inputs,
+    # mask and y against the oracle, layer by layer
+    for layer in range(workloads()["c3_b1"].n_layers):
+        print(f"[fullsize] c3_b1 layer {layer} start", flush=True)
+        _run("c3_b1", layer)
+
+
+@pytest.mark.parametrize("name,layer", [("c3_b4", 0), ("c3_b16", 0), ("c3_b4", 1), ("c3_b16", 1)])
 def test_c3_llama3_8b_stack(name, layer):
     c, wl = _run(name, layer)
-    if wl.batch >= 4:
-        _permuted(c, wl, layer)
+    _permuted(c, wl, layer)
 
 
 @pytest.mark.parametrize("layer", [0, 1])

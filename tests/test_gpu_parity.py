@@ -192,3 +192,42 @@ def test_measurement_events(B):
         assert torch.equal(u, v)
     times = [ev[p].elapsed_time(ev[p + 1]) for p in range(P.N_PHASES)]
     assert all(0.0 < t < 1000.0 for t in times), times
+
+
+@pytest.mark.parametrize("B,kind", [(1, "int4"), (2, "int8"), (8, "int4"), (8, "int8")])
+def test_graph_replay(B, kind):
+    # one forward captured in a HIP graph and replayed several times with new
+    # x and eager work between the replays; every replay equals an eager call
+    # bit for bit (int4 splits proxy tiles across blocks, so the per-tile
+    # arrival counters must be left clear by every call)
+    import free_ffn_activation_prox_amd as P
+    d, F = 1024, 1000
+    c = _case(d, F, B, seed=60 + B, kind=kind)
+    k_in, k_ff = pct_count(d, 60), pct_count(F, 30)
+    dev = c.dx.device
+    xbuf = c.dx.clone()
+    y = torch.empty(B, d, dtype=torch.float32, device=dev)
+    mask = torch.empty(B, F, dtype=torch.uint8, device=dev)
+    idx = torch.empty(B, k_ff, dtype=torch.int32, device=dev)
+    ws = P.alloc_workspace(d, F, B, kind)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        P.ffn_forward(xbuf, c.weights, c.proxy, k_in, k_ff, y=y, mask=mask, idx=idx, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        P.ffn_forward(xbuf, c.weights, c.proxy, k_in, k_ff, y=y, mask=mask, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(B)
+    for rep in range(4):
+        xnew = (torch.randn(B, d, generator=gen) * 2.0).to(torch.bfloat16).to(dev)
+        xbuf.copy_(xnew)
+        g.replay()
+        torch.cuda.synchronize()
+        ye, me, ie = P.ffn_forward(xnew, c.weights, c.proxy, k_in, k_ff)
+        torch.cuda.synchronize()
+        assert torch.equal(mask, me) and torch.equal(idx, ie), f"replay {rep}: mask differs"
+        assert torch.equal(y, ye), f"replay {rep}: y differs"
+
