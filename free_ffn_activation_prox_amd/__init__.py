@@ -73,6 +73,9 @@ def _load() -> ctypes.CDLL:
                                    P, P, P, P, SZ, P]),
         "prox_ffn_forward_taps": (I32, [P, I32, ctypes.POINTER(_Weights), ctypes.POINTER(_Proxy), I32,
                                         I32, P, P, P, P, SZ, ctypes.POINTER(_Taps), P]),
+        "prox_noalloc_scratch_bytes": (SZ, []),
+        "prox_ffn_forward_noalloc": (I32, [P, I32, ctypes.POINTER(_Weights), ctypes.POINTER(_Proxy), I32, I32,
+                                           P, P, P, P]),
         "prox_status_str": (ctypes.c_char_p, [I32]),
         "prox_last_error": (ctypes.c_char_p, []),
     }
@@ -241,5 +244,31 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     return y, mask, idx[:, :k_ff]
 
 
-__all__ = ["Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
+def noalloc_scratch_bytes() -> int:
+    return _lib.prox_noalloc_scratch_bytes()
+
+
+def ffn_forward_noalloc(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y, mask, idx,
+                        stream=None):
+    """prox_ffn_forward_noalloc: the forward with the library's fixed device
+    scratch as workspace (no allocation in the call).  y, mask and idx are the
+    caller's ([B][d] fp32, [B][F] uint8, [B][>= max(k_ff, 1)] int32)."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
+    B, d = x.shape
+    for t, dt, shape in ((y, torch.float32, (B, d)), (mask, torch.uint8, (B, weights.d_ff))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError("y / mask: wrong dtype, shape or layout")
+    if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != B or idx.shape[1] < max(k_ff, 1) \
+            or not idx.is_contiguous():
+        raise ValueError("idx must be int32 [B][>= max(k_ff, 1)]")
+    _check(_lib.prox_ffn_forward_noalloc(x.data_ptr(), B, ctypes.byref(weights._c), ctypes.byref(proxy.desc),
+                                         k_in, k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(),
+                                         _stream_ptr(stream)),
+           "prox_ffn_forward_noalloc")
+    return y, mask, idx[:, :k_ff]
+
+
+__all__ = ["noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
            "build_proxy", "alloc_workspace", "ffn_forward", "LIB_PATH", "KINDS", "N_PHASES", "PHASES"]

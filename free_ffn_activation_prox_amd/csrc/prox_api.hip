@@ -4,6 +4,7 @@
 #include <chrono>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "prox.h"
@@ -244,6 +245,66 @@ extern "C" prox_status prox_ffn_forward(const void* x, int32_t batch, const prox
                                         size_t ws_bytes, void* stream) {
     return prox_ffn_forward_taps(x, batch, w, p, k_in, k_ff, y, mask, idx, workspace, ws_bytes,
                                  nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a fixed device array of this
+// library, one copy per GPU, held until the process ends.  Its address on the
+// current device comes from hipGetSymbolAddress the first time a call runs on
+// that device (the array's name in host code is not a device address).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = PROX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of `scratch` on the current device, or null (error set).
+void* scratch_on_current_device(prox_status* st) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *st = hip_fail(e, "hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *st = fail(PROX_E_UNSUPPORTED, "device id %d above the %d devices this library tracks", dev, kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *st = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t prox_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" prox_status prox_ffn_forward_noalloc(const void* x, int32_t batch, const prox_weights* w,
+                                                const prox_proxy* p, int32_t k_in, int32_t k_ff, float* y,
+                                                uint8_t* mask, int32_t* idx, void* stream) {
+    g_err.clear();
+    if (!w || !p) return fail(PROX_E_INVALID, "null weights or proxy");
+    const size_t need = prox_workspace_bytes(w->d_model, w->d_ff, batch, p->kind);
+    if (need > kScratchBytes)
+        return fail(PROX_E_UNSUPPORTED, "this shape needs a %zu-byte workspace, above the %zu-byte scratch of the "
+                    "allocation-free forward; use prox_ffn_forward with a caller workspace", need, kScratchBytes);
+    prox_status st = PROX_OK;
+    void* ws = scratch_on_current_device(&st);
+    if (!ws) return st;
+    // need == 0 (invalid shape or batch): prox_ffn_forward_taps reports it
+    return prox_ffn_forward_taps(x, batch, w, p, k_in, k_ff, y, mask, idx, ws, kScratchBytes, nullptr, stream);
 }
 
 extern "C" const char* prox_status_str(int32_t st) {

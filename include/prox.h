@@ -176,6 +176,30 @@ prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const prox_weigh
                                   uint8_t* mask, int32_t* idx, void* workspace, size_t ws_bytes,
                                   const prox_taps* taps, void* stream);
 
+/* ---- Allocation-free forward ----------------------------------------------
+ * For callers that cannot allocate device memory around a forward (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * prox_ffn_forward with the workspace taken from a fixed device array of the
+ * library, PROX_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, allocated when the
+ * library is loaded and held until the process ends.  No call allocates.
+ *   Arguments as prox_ffn_forward, without the workspace.
+ *   Returns PROX_E_UNSUPPORTED (nothing enqueued) when this shape and batch
+ *   need more workspace than the array holds (prox_workspace_bytes above
+ *   PROX_NOALLOC_SCRATCH_BYTES), PROX_E_HIP if the array's address on the
+ *   current device cannot be found; otherwise as prox_ffn_forward.
+ *   Every call on one GPU uses that GPU's array: calls that overlap in time
+ *   on one GPU (other streams, other host threads) race and must not be
+ *   issued.  The array keeps the last call's contents; the forward needs
+ *   none of it cleared (as for any workspace).                               */
+#define PROX_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Bytes of the allocation-free forward's scratch array (per GPU). */
+size_t prox_noalloc_scratch_bytes(void);
+
+prox_status prox_ffn_forward_noalloc(const void* x, int32_t batch, const prox_weights* w,
+                                     const prox_proxy* p, int32_t k_in, int32_t k_ff, float* y,
+                                     uint8_t* mask, int32_t* idx, void* stream);
+
 /* Static text for a status code. */
 const char* prox_status_str(int32_t status);
 

@@ -117,3 +117,17 @@ def test_build_proxy_validation():
     assert _lib.prox_build_proxy(None, 1, FAKE, 1 << 30, ctypes.byref(out), None) == INVALID
     w4 = _Weights(520, 64, FAKE, FAKE, FAKE)
     assert _lib.prox_build_proxy(ctypes.byref(w4), 2, FAKE, 1 << 30, ctypes.byref(out), None) == INVALID
+
+
+def test_noalloc_rejects_oversized_shape_before_any_launch():
+    # d_model 16384, d_ff 32768, 64 tokens need far more than the 32 MiB
+    # scratch: rejected on the host (no device pointer is touched)
+    assert P.noalloc_scratch_bytes() == 32 << 20
+    assert P.workspace_bytes(16384, 32768, 64, "int8") > P.noalloc_scratch_bytes()
+    w = _Weights(16384, 32768, FAKE, FAKE, FAKE)
+    p = _Proxy()
+    p.kind, p.d_model, p.d_ff = 1, 16384, 32768
+    st = _lib.prox_ffn_forward_noalloc(FAKE, 64, ctypes.byref(w), ctypes.byref(p), 100, 100,
+                                       FAKE, FAKE, FAKE, None)
+    assert st == UNSUPPORTED
+    assert b"scratch" in _lib.prox_last_error()
