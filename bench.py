@@ -1,17 +1,21 @@
-"""Bench: Prox sparse SwiGLU FFN layer on one MI355X.
+"""Bench: Prox sparse SwiGLU FFN on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2_s70]
 
-A step is one prox_ffn_forward (Stage 1 + Stage 2, every phase of the path)
-over one batch of synthetic tokens for one FFN layer.  Inputs are resident in
-HBM before timing starts.  Several copies of the layer's weights and proxy at
-distinct addresses are rotated step by step so no step finds its weights in
-the 256 MB last-level cache; x changes every step, so masks change too.
+A step is one pass of the whole path over one batch of synthetic tokens:
+prox_ffn_forward (Stage 1 + Stage 2, every kernel of the path) for one FFN
+layer, or, for the stacked workloads (c3_*: 32 layers, c5: 64 layers), for
+every layer of the stack in order (µs per token = stack time / batch).
+Inputs are resident in HBM before timing starts.  Single-layer workloads
+rotate several copies of the layer's weights and proxy at distinct addresses
+so no step finds its weights in the 256 MB last-level cache (a stack is
+larger than the cache by itself); x changes every step, so masks change too.
 
-Prints ONE JSON line: the layer throughput in algorithmic HBM GB/s (the
-metric's unit), microseconds per token, the roofline entry of the dominant
-kernel (timed live with events on the launch stream) and the CPU oracle
-timed on a bounded sample of the same workload.
+Prints ONE JSON line: the throughput in algorithmic HBM GB/s (the metric's
+unit), µs per token, the roofline entry of the dominant kernel (timed live
+with events on the launch stream), the read rate of a plain streaming kernel
+on the same GPU (the practical ceiling) and the CPU oracle timed on a bounded
+sample of the same workload, with one thread and with every core.
 """
 
 from __future__ import annotations
@@ -39,11 +43,11 @@ LLC_BYTES = 256 << 20
 BATCH_MIN = 4   # the library's switch to the matrix-core path (tokens per call)
 
 
-def algorithmic_bytes(d, F, kind, k_in_rows, k_ch, B):
+def algorithmic_bytes(d, F, kind, k_in_rows, k_ch):
     """Weight bytes one forward must read at minimum: proxy codes of the kept
     rows + proxy scales (Stage 1) and 3 bf16 rows per kept channel (Stage 2).
-    For B > 1 the kept rows / channels are the union over the batch (measured
-    from the call's own outputs)."""
+    For several tokens the kept rows / channels are the union over the batch
+    (measured from the call's own outputs)."""
     bits = 8 if kind == "int8" else 4
     groups = 1 if kind == "int8" else d // 128
     proxy = 2 * k_in_rows * F * bits // 8 + 2 * groups * F * 4
@@ -57,21 +61,22 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2_s70")
+    ap.add_argument("--layers", type=int, default=0, help="stacked workloads: first N layers only (0 = all)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="per CPU leg")
+    ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, --steps times (the reference "
                          "for scaling hardware byte counters)")
     args = ap.parse_args(argv)
 
-    if args.copy_calibration:
-        return copy_calibration(args.copy_calibration, args.steps)
-
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding plan is design-only.", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
 
     import torch
     import free_ffn_activation_prox_amd as P
@@ -81,38 +86,57 @@ def main(argv=None):
     torch.cuda.set_device(dev)
 
     wl = workloads()[args.workload]
-    layer = 0
-    d, F = wl.layers[layer].d, wl.layers[layer].F
+    n_layers = wl.n_layers if not args.layers else min(args.layers, wl.n_layers)
+    stack = wl.n_layers > 1
     B, kind = wl.batch, wl.proxy
-    k_in, k_ff = wl.k_in(layer), wl.k_ff(layer)
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     t0 = time.time()
-    w = gen_weights(wl.config_id, layer, d, F)
-    base = P.Weights(up(w["wg_t"]), up(w["wu_t"]), up(w["wd"]))
-    base_proxy = P.build_proxy(base, kind)
-    layer_bytes = 3 * F * d * 2 + base_proxy.desc.bytes
-    copies = args.copies or max(4, int(np.ceil(4 * LLC_BYTES / layer_bytes)))
-    copies = min(copies, 64)
-    sets = [(base, base_proxy)]
-    for _ in range(copies - 1):
-        wc = P.Weights(base.w_gate_t.clone(), base.w_up_t.clone(), base.w_down.clone())
-        sets.append((wc, P.build_proxy(wc, kind)))
+    # per layer: a list of (weights, proxy) copies; single layers rotate copies
+    sets, w0 = [], None
+    for layer in range(n_layers):
+        d, F = wl.layers[layer].d, wl.layers[layer].F
+        w = gen_weights(wl.config_id, layer, d, F)
+        if layer == 0:
+            w0 = w
+        base = P.Weights(up(w["wg_t"]), up(w["wu_t"]), up(w["wd"]))
+        copies_l = [(base, P.build_proxy(base, kind))]
+        if not stack:
+            layer_bytes = 3 * F * d * 2 + copies_l[0][1].desc.bytes
+            copies = args.copies or max(4, int(np.ceil(4 * LLC_BYTES / layer_bytes)))
+            for _ in range(min(copies, 64) - 1):
+                wc = P.Weights(base.w_gate_t.clone(), base.w_up_t.clone(), base.w_down.clone())
+                copies_l.append((wc, P.build_proxy(wc, kind)))
+        sets.append(copies_l)
+        del w
+    n_copies = len(sets[0])
     n_x = 16
-    xs = [up(gen_x(wl, layer, step=s)) for s in range(n_x)]
-    ws = P.alloc_workspace(d, F, B, kind, dev)
-    y = torch.empty(B, d, dtype=torch.float32, device=dev)
-    mask = torch.empty(B, F, dtype=torch.uint8, device=dev)
-    idx = torch.empty(B, max(k_ff, 1), dtype=torch.int32, device=dev)
+    xs = [[up(gen_x(wl, layer, step=s)) for s in range(n_x)] for layer in range(n_layers)]
+    shapes = sorted({(wl.layers[l].d, wl.layers[l].F) for l in range(n_layers)})
+    ws = P.alloc_workspace(max(s[0] for s in shapes), max(s[1] for s in shapes), B, kind, dev)
+    ws_need = max(P.workspace_bytes(d, F, B, kind) for d, F in shapes)
+    assert ws.numel() >= ws_need
+    bufs = {}
+    for d, F in shapes:
+        k_ff_max = max(wl.k_ff(l) for l in range(n_layers) if (wl.layers[l].d, wl.layers[l].F) == (d, F))
+        bufs[(d, F)] = (torch.empty(B, d, dtype=torch.float32, device=dev),
+                        torch.empty(B, F, dtype=torch.uint8, device=dev),
+                        torch.empty(B, max(k_ff_max, 1), dtype=torch.int32, device=dev))
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
+    def forward(layer, i, events=None):
+        d, F = wl.layers[layer].d, wl.layers[layer].F
+        wt, px = sets[layer][i % n_copies]
+        y, mask, idx = bufs[(d, F)]
+        P.ffn_forward(xs[layer][i % n_x], wt, px, wl.k_in(layer), wl.k_ff(layer), y=y, mask=mask, idx=idx,
+                      workspace=ws[:P.workspace_bytes(d, F, B, kind)], events=events)
+
     def step(i, events=None):
-        wt, px = sets[i % copies]
-        P.ffn_forward(xs[i % n_x], wt, px, k_in, k_ff, y=y, mask=mask, idx=idx, workspace=ws,
-                      events=events)
+        for layer in range(n_layers):
+            forward(layer, i, None if events is None else events[layer])
 
     for i in range(args.warmup):
         step(i)
@@ -131,34 +155,45 @@ def main(argv=None):
     ms_per_step = total_ms / K
 
     # per-kernel durations: the same K steps again, with events at every phase
-    # boundary recorded by the library on its launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(P.N_PHASES + 1)] for _ in range(K)]
+    # boundary of every layer, recorded by the library on its launch stream
+    Kp = min(K, max(1, 400 // n_layers))
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(P.N_PHASES + 1)] for _ in range(n_layers)]
+          for _ in range(Kp)]
     for row in ev:              # torch creates the HIP event on first record
-        for e in row:
-            e.record()
+        for lay in row:
+            for e in lay:
+                e.record()
     torch.cuda.synchronize()
-    for i in range(K):
+    for i in range(Kp):
         step(args.warmup + i, ev[i])
     torch.cuda.synchronize()
-    phase_ms = np.zeros(P.N_PHASES)
-    for i in range(K):
-        for p in range(P.N_PHASES):
-            phase_ms[p] += ev[i][p].elapsed_time(ev[i][p + 1])
-    phase_ms /= K
+    phase_ms = np.zeros(P.N_PHASES)        # per step (summed over the layers)
+    for i in range(Kp):
+        for lay in ev[i]:
+            for p in range(P.N_PHASES):
+                phase_ms[p] += lay[p].elapsed_time(lay[p + 1])
+    phase_ms /= Kp
 
-    # union of kept rows / channels over the batch, from the outputs of one call
-    step(0)
-    torch.cuda.synchronize()
-    m = mask.cpu().numpy().astype(bool)
-    ch_union = int(m.any(axis=0).sum())
-    if B == 1:
-        rows_union = k_in
-    else:
-        xb = xs[0].float().abs().cpu().numpy()
-        order = np.lexsort((np.tile(np.arange(d), (B, 1)), -xb), axis=1)[:, :k_in]
-        rows_union = int(len(np.unique(order)))
-    proxy_b, stage2_b = algorithmic_bytes(d, F, kind, rows_union, ch_union, B)
-    io_b = B * (2 * d + 4 * d + F + 4 * k_ff)       # x, y, mask, idx
+    # algorithmic bytes: per layer, union of kept rows / channels over the
+    # batch from the outputs of one call
+    proxy_b = stage2_b = io_b = 0
+    for layer in range(n_layers):
+        d, F = wl.layers[layer].d, wl.layers[layer].F
+        k_in, k_ff = wl.k_in(layer), wl.k_ff(layer)
+        forward(layer, 0)
+        torch.cuda.synchronize()
+        m = bufs[(d, F)][1].cpu().numpy().astype(bool)
+        ch_union = int(m.any(axis=0).sum())
+        if B == 1:
+            rows_union = k_in
+        else:
+            xb = xs[layer][0].float().abs().cpu().numpy()
+            order = np.lexsort((np.tile(np.arange(d), (B, 1)), -xb), axis=1)[:, :k_in]
+            rows_union = int(len(np.unique(order)))
+        pb, sb = algorithmic_bytes(d, F, kind, rows_union, ch_union)
+        proxy_b += pb
+        stage2_b += sb
+        io_b += B * (2 * d + 4 * d + F + 4 * k_ff)       # x, y, mask, idx
     total_b = proxy_b + stage2_b + io_b
     gbs = total_b / (ms_per_step * 1e-3) / 1e9
     us_tok = ms_per_step * 1e3 / B
@@ -174,8 +209,11 @@ def main(argv=None):
     if B < BATCH_MIN:
         dom_kernel = {0: "k_stage1", 1: "k_stage2"}.get(dom, "k_reduce_y")
     else:
-        dom_kernel = {0: "xsel + k_proxy_batch", 1: "k_stage2 (selection) + k_gateup_batch + k_down_batch"}.get(dom, "k_reduce_y")
-    traffic = measured_traffic(wl.name, dom_kernel) if B < BATCH_MIN else None
+        dom_kernel = {0: "k_xsel + k_proxy_batch",
+                      1: "k_stage2 (selection) + k_gateup_batch + k_down_batch"}.get(dom, "k_reduce_y")
+    src_hash = kernel_sources_hash()
+    prof = committed_profile(wl.name, dom_kernel, src_hash, n_layers)
+    probe = None if args.no_read_probe else read_probe_gbs(P, torch, dev)
 
     out = {
         "metric": METRIC,
@@ -188,29 +226,69 @@ def main(argv=None):
         "us_per_token": round(us_tok, 3),
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "pct_of_read_probe": round(100.0 * gbs / probe, 2) if probe else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "dtype_detail": "Stage 2: bf16 weights, fp32 accumulation; Stage 1: int8/int4 codes x bf16 x, fp64 accumulation",
-        "data": "synthetic (seeded N(0,0.02) bf16 weights, Laplace x with outliers; random-init, no checkpoint)",
-        "config": {"workload": f"{wl.name}: d_model={d} d_ff={F} batch={B} proxy={kind} "
-                               f"keep={wl.keep_pct}% sparsity={wl.sparsity_pct}%",
-                   "d_model": d, "d_ff": F, "batch": B, "proxy": kind, "k_in": k_in, "k_ff": k_ff,
-                   "weight_copies_rotated": copies, "algorithmic_bytes_per_step": int(total_b)},
+        "dtype_detail": "Stage 2: bf16 weights, fp32 accumulation; Stage 1: int8/int4 codes x bf16 x, "
+                        "fp32 exact chunk sums into fp64 totals",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, Laplace x with outliers or RMS-normalised; "
+                "random-init, no checkpoint)",
+        "config": {"workload": f"{wl.name}: d_model={'/'.join(str(s[0]) for s in shapes)} "
+                               f"d_ff={'/'.join(str(s[1]) for s in shapes)} layers={n_layers} batch={B} "
+                               f"proxy={kind} keep={wl.keep_pct}% sparsity={wl.sparsity_pct}%",
+                   "layers": n_layers, "batch": B, "proxy": kind,
+                   "k_in": [wl.k_in(l) for l in range(min(n_layers, 2))],
+                   "k_ff": [wl.k_ff(l) for l in range(min(n_layers, 2))],
+                   "weight_copies_rotated": n_copies, "algorithmic_bytes_per_step": int(total_b)},
         "phase_us": {P.PHASES[p]: round(float(phase_ms[p] * 1e3), 2) for p in range(P.N_PHASES)},
         "roofline": {"bound": "hbm", "kernel": dom_kernel, "phase": dom_name, "achieved": round(dom_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": int(dom_bytes),
+                     "traffic": prof.get("traffic"), "algorithmic_bytes": int(dom_bytes),
+                     "timing": "phase events on the launch stream (include the dispatch gap before the kernel)",
+                     "rocprof_avg_us": prof.get("avg_us"),
+                     "achieved_rocprof": round(dom_bytes / n_layers / (prof["avg_us"] * 1e-6) / 1e9, 1)
+                     if prof.get("avg_us") else None,
+                     "frac_rocprof": round(dom_bytes / n_layers / (prof["avg_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                     if prof.get("avg_us") else None,
+                     "profile": prof.get("file"),
                      "layer_achieved": round(gbs, 1), "layer_frac": round(gbs / PEAK_HBM_GBS, 4)},
-        "kernel_sources_sha256": kernel_sources_hash(),
+        "read_probe_GBps": round(probe, 1) if probe else None,
+        "kernel_sources_sha256": src_hash,
+        "library": {"path": os.path.relpath(P.LIB_PATH, ROOT), "sha256": P.library_sha256()},
         "setup_s": round(setup_s, 1),
     }
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, layer, w, xs, k_in, k_ff, total_b / B, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, w0, xs[0], total_b / n_layers / B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def read_probe_gbs(P, torch, dev, gib=2, reps=10):
+    """Read rate of a plain streaming kernel over `gib` GiB (eight times the
+    last-level cache, so the reads come from HBM): the practical ceiling.  The
+    best median over a few grid sizes."""
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    best = 0.0
+    for blocks in (256, 512, 1024, 2048):
+        sink = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            P.read_probe(buf, sink, blocks)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            P.read_probe(buf, sink, blocks)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        best = max(best, n / (float(np.median(times)) * 1e-3) / 1e9)
+    del buf
+    return best
 
 
 def kernel_sources_hash():
@@ -226,23 +304,43 @@ def kernel_sources_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary of
-    this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the plain-copy
-    factor), or None when there is none or the kernel sources have changed
-    since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"prox_forward_{workload}_hbm_bytes.md")
-    if not os.path.exists(path):
-        return None
-    text = open(path).read()
-    m = re.search(r"Kernel sources sha256: ([0-9a-f]+)", text)
-    if not m or m.group(1) != kernel_sources_hash():
-        return None
-    for line in text.splitlines():
-        cells = [c.strip() for c in line.split("|")]
-        if len(cells) > 7 and f"prox::{kernel}<" in cells[1]:
-            return int(round((float(cells[5]) + float(cells[6])) * 1e6))
-    return None
+def committed_profile(workload, kernel, src_hash, n_layers):
+    """rocprofv3 figures of the dominant kernel from the committed summaries of
+    this workload (profiles/prox_forward_<workload>_kernel_stats.md and
+    _hbm_bytes.md), used only while the kernel sources match the ones they were
+    taken on: average kernel duration (µs) and HBM bytes per launch (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the plain-copy factor).  Empty when there is no
+    matching summary."""
+    out = {}
+    names = [k.strip() for k in kernel.split("+")]
+    if len(names) != 1 or n_layers != 1:
+        return out            # several kernels per phase, or a stack: no single-kernel figure
+    pat = f"prox::{names[0]}<" if "<" not in names[0] else names[0]
+
+    def rows(path):
+        if not os.path.exists(path):
+            return None
+        text = open(path).read()
+        m = re.search(r"Kernel sources sha256: ([0-9a-f]+)", text)
+        if not m or m.group(1) != src_hash:
+            return None
+        return [[c.strip() for c in line.split("|")] for line in text.splitlines() if line.startswith("|")]
+
+    base = os.path.join(ROOT, "profiles", f"prox_forward_{workload}")
+    st = rows(base + "_kernel_stats.md")
+    if st:
+        for cells in st:
+            if len(cells) > 4 and (pat in cells[1] or f"prox::{names[0]}(" in cells[1]):
+                out["avg_us"] = float(cells[3])
+                out["file"] = os.path.relpath(base + "_kernel_stats.md", ROOT)
+                break
+    hb = rows(base + "_hbm_bytes.md")
+    if hb:
+        for cells in hb:
+            if len(cells) > 7 and (pat in cells[1] or f"prox::{names[0]}(" in cells[1]):
+                out["traffic"] = int(round((float(cells[5]) + float(cells[6])) * 1e6))
+                break
+    return out
 
 
 def copy_calibration(mib, steps):
@@ -269,33 +367,53 @@ def copy_calibration(mib, steps):
     return 0
 
 
-def cpu_baseline(wl, layer, w, xs, k_in, k_ff, bytes_per_token, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    tokens of the same layer, one oracle forward each, until about budget_s."""
-    from oracle import prox_oracle as O
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, w, xs, bytes_per_token, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    single-token forwards of layer 0, one token each, for about budget_s with
+    one BLAS thread and again with every core."""
+    from oracle import prox_oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
     f64 = O.bf16_bits_to_f64
     wg, wu, wd = f64(w["wg_t"]), f64(w["wu_t"]), f64(w["wd"])
     proxies = (O.build_proxy(wg.T, wl.proxy), O.build_proxy(wu.T, wl.proxy))
-    xs_h = [f64(x.view(__import__("torch").int16).cpu().numpy().view(np.uint16)) for x in xs]
-    n = 0
-    t0 = time.time()
-    while True:
-        xb = xs_h[n % len(xs_h)][:1]
-        O.oracle_forward(xb, wg, wu, wd, wl.proxy, k_in, k_ff, proxies=proxies)
-        n += 1
-        if time.time() - t0 >= budget_s:
-            break
-    dt = time.time() - t0
-    per_tok = dt / n
-    return {"value": round(bytes_per_token / per_tok / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "us_per_token": round(per_tok * 1e6, 1),
-            "sample": f"{n} single-token oracle forwards of {wl.name} layer {layer} "
-                      f"(float64 numpy, proxies prebuilt), {dt:.1f} s"}
+    import torch
+    xs_h = [f64(x.view(torch.int16).cpu().numpy().view(np.uint16)) for x in xs]
+    k_in, k_ff = wl.k_in(0), wl.k_ff(0)
+
+    def leg(threads):
+        with threadpool_limits(limits=threads):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            n = 0
+            t0 = time.time()
+            while True:
+                O.oracle_forward(xs_h[n % len(xs_h)][:1], wg, wu, wd, wl.proxy, k_in, k_ff, proxies=proxies)
+                n += 1
+                if time.time() - t0 >= budget_s:
+                    break
+            dt = time.time() - t0
+        return n, dt, used
+
+    all_cores = os.cpu_count() or 1
+    n1, dt1, used1 = leg(1)
+    nN, dtN, usedN = leg(all_cores)
+    per1, perN = dt1 / n1, dtN / nN
+    return {"value": round(bytes_per_token / perN / 1e9, 4), "unit": "GB/s", "cores": int(usedN),
+            "kind": "oracle", "us_per_token": round(perN * 1e6, 1), "cpu_model": cpu_model(),
+            "host_cpus": all_cores,
+            "single_thread": {"value": round(bytes_per_token / per1 / 1e9, 4), "unit": "GB/s", "cores": int(used1),
+                              "us_per_token": round(per1 * 1e6, 1)},
+            "sample": f"single-token oracle forwards of {wl.name} layer 0 (float64 numpy, proxies prebuilt): "
+                      f"{nN} in {dtN:.1f} s on {usedN} threads, {n1} in {dt1:.1f} s on 1 thread"}
 
 
 if __name__ == "__main__":

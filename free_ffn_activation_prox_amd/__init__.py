@@ -76,6 +76,7 @@ def _load() -> ctypes.CDLL:
         "prox_noalloc_scratch_bytes": (SZ, []),
         "prox_ffn_forward_noalloc": (I32, [P, I32, ctypes.POINTER(_Weights), ctypes.POINTER(_Proxy), I32, I32,
                                            P, P, P, P]),
+        "prox_read_probe": (I32, [P, SZ, P, I32, P]),
         "prox_status_str": (ctypes.c_char_p, [I32]),
         "prox_last_error": (ctypes.c_char_p, []),
     }
@@ -244,6 +245,15 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     return y, mask, idx[:, :k_ff]
 
 
+def read_probe(buf, sink, blocks: int, stream=None) -> None:
+    """Measurement helper: one plain streaming read of the device tensor `buf`
+    (prox_read_probe); `sink` is an int32/uint32 device tensor of blocks * 512."""
+    if sink.numel() < blocks * 512:
+        raise ValueError("sink needs blocks * 512 words")
+    _check(_lib.prox_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), blocks,
+                                _stream_ptr(stream)), "prox_read_probe")
+
+
 def noalloc_scratch_bytes() -> int:
     return _lib.prox_noalloc_scratch_bytes()
 
@@ -270,5 +280,5 @@ def ffn_forward_noalloc(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int,
     return y, mask, idx[:, :k_ff]
 
 
-__all__ = ["noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
+__all__ = ["read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
            "build_proxy", "alloc_workspace", "ffn_forward", "LIB_PATH", "KINDS", "N_PHASES", "PHASES"]

@@ -200,6 +200,17 @@ prox_status prox_ffn_forward_noalloc(const void* x, int32_t batch, const prox_we
                                      const prox_proxy* p, int32_t k_in, int32_t k_ff, float* y,
                                      uint8_t* mask, int32_t* idx, void* stream);
 
+/* ---- Measurement helper (not part of the forward) ---------------------------
+ * Read-stream probe: reads the first bytes / 16 * 16 bytes of the device
+ * buffer `buf` (16-byte aligned) with `blocks` blocks of 512 threads, each
+ * block one contiguous part, 16-byte loads, eight in flight per thread
+ * (64 KB per block), and writes one word per thread to the
+ * device array sink[blocks * 512] (so the loads are not removed).  Timing it
+ * gives the HBM read rate a plain stream reaches, the practical ceiling the
+ * forward's rate is compared with.  PROX_E_INVALID for a null or misaligned
+ * buffer, bytes < 16 or blocks < 1.                                         */
+prox_status prox_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
 /* Static text for a status code. */
 const char* prox_status_str(int32_t status);
 
