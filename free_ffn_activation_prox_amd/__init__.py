@@ -51,7 +51,7 @@ class _Proxy(ctypes.Structure):
 class _Taps(ctypes.Structure):
     _fields_ = [("in_idx", ctypes.c_void_p), ("key", ctypes.c_void_p), ("h_hat", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("stream_idx", ctypes.c_void_p)]
+                ("reserved", ctypes.c_int32), ("stream_idx", ctypes.c_void_p), ("timeline", ctypes.c_void_p)]
 
 
 N_PHASES = 3
@@ -216,7 +216,7 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     sp = _stream_ptr(stream)
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*[getattr(e, "cuda_event", e) for e in events])
-        ct = _Taps(None, None, None, arr, len(events), 0, None)
+        ct = _Taps(None, None, None, arr, len(events), 0, None, None)
         _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
                                           ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),
                                           mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
@@ -229,7 +229,7 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
              "h_hat": torch.empty(B, F, dtype=torch.float64, device=dev),
              "stream_idx": torch.full((B, max(k_ff, 1)), -1, dtype=torch.int32, device=dev)}
         ct = _Taps(t["in_idx"].data_ptr(), t["key"].data_ptr(), t["h_hat"].data_ptr(), None, 0, 0,
-                   t["stream_idx"].data_ptr())
+                   t["stream_idx"].data_ptr(), None)
         _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
                                           ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),
                                           mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
@@ -252,6 +252,21 @@ def read_probe(buf, sink, blocks: int, stream=None) -> None:
         raise ValueError("sink needs blocks * 512 words")
     _check(_lib.prox_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), blocks,
                                 _stream_ptr(stream)), "prox_read_probe")
+
+
+def timeline_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y, mask, idx, workspace,
+                     stream=None):
+    """Measurement hook: the forward with the per-block timeline tap; returns
+    the uint64 device tensor [2][1024][8] of 100 MHz counter stamps."""
+    import torch
+    tl = torch.zeros(2 * 1024 * 8, dtype=torch.int64, device=x.device)
+    ct = _Taps(None, None, None, None, 0, 0, None, tl.data_ptr())
+    B = x.shape[0]
+    _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c), ctypes.byref(proxy.desc), k_in,
+                                      k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), ctypes.byref(ct), _stream_ptr(stream)),
+           "prox_ffn_forward_taps")
+    return tl.view(2, 1024, 8)
 
 
 def noalloc_scratch_bytes() -> int:
@@ -280,5 +295,5 @@ def ffn_forward_noalloc(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int,
     return y, mask, idx[:, :k_ff]
 
 
-__all__ = ["read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
+__all__ = ["timeline_forward", "read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
            "build_proxy", "alloc_workspace", "ffn_forward", "LIB_PATH", "KINDS", "N_PHASES", "PHASES"]

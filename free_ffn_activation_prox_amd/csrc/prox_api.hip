@@ -226,11 +226,11 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     double* part = reinterpret_cast<double*>(ws + L.part);
     e = launch_stage1(xb, batch, d, k_in, pv, key, part, tcnt, next_call_tag(), g1,
                       taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr,
-                      taps ? taps->in_idx : nullptr, s);
+                      taps ? taps->in_idx : nullptr, taps ? (unsigned long long*)taps->timeline : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "stage 1");
     if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_stage2(xb, wg, wu, wd, key, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart,
-                      taps ? taps->stream_idx : nullptr, s);
+                      taps ? taps->stream_idx : nullptr, taps ? (unsigned long long*)taps->timeline : nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "stage 2");
     if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_reduce_y(ypart, batch, d, W2, y, s);

@@ -57,6 +57,14 @@ __device__ __forceinline__ int tile_arrive(unsigned long long* cnt, uint32_t gen
     }
 }
 
+// Measurement hook: thread 0 of the block stores the 100 MHz real-time
+// counter at one of eight points of kernel `kern` (timeline layout
+// [kern][1024 blocks][8 points], block = blockIdx.y * gridDim.x + blockIdx.x).
+__device__ __forceinline__ void tl_mark(unsigned long long* tl, int kern, int point) {
+    if (tl && threadIdx.x == 0)
+        tl[((size_t)kern * 1024 + blockIdx.y * gridDim.x + blockIdx.x) * 8 + point] = __builtin_amdgcn_s_memrealtime();
+}
+
 // Number of set bits of `m` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -128,11 +128,11 @@ hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d,
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
                          double* part, unsigned long long* tcnt, uint32_t gen,
                          const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
-                         hipStream_t s);
+                         unsigned long long* tl, hipStream_t s);
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
                          const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
                          int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, int32_t* stream_tap,
-                         hipStream_t s);
+                         unsigned long long* tl, hipStream_t s);
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s);
 // Stage-2 selection only: mask (required) and idx (nullable) from the keys.
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,

@@ -24,6 +24,9 @@
 namespace prox {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// Signed fields by shifts.  (__builtin_amdgcn_sbfe converted to double was
+// lowered here as an unsigned conversion, so negative fields came out as
+// ~4e9: every signed field below is extracted this way.)
 __device__ __forceinline__ int sext8(uint32_t w, int c) { return (int)(w << (24 - 8 * c)) >> 24; }
 __device__ __forceinline__ int sext4(uint32_t w, int c) { return (int)(w << (28 - 4 * c)) >> 28; }
 
@@ -160,6 +163,7 @@ struct Stage1Args {
     int32_t* in_idx_tap; // [B][k_in] or null
     int tiles, nch, nb1;
     uint32_t gen;        // tag of this call, distinct from earlier calls
+    unsigned long long* tl;   // timeline stamps or null
 };
 
 constexpr int kS1Threads = 512;
@@ -520,7 +524,9 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     const int k_in = a.k_in, d = a.d, nch = a.nch;
     uint32_t* list = dyn;                         // [k_in + 64], then the chunks' exactness flags
     const uint8_t* xflags = reinterpret_cast<const uint8_t*>(dyn + s1_flags_off(k_in));
+    tl_mark(a.tl, 0, 0);
     stage1_select<PX>(a, b, list, hist, sc);
+    tl_mark(a.tl, 0, 1);
     bool flags_done = false;     // the chunk flags are computed under the block's first loads
 
     const long long T = (long long)a.tiles * nch;
@@ -603,6 +609,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
                 au[c] = ou[c];
             }
         }
+        tl_mark(a.tl, 0, 2);
         // reduce the 8 row slots of the wave (lanes l ^ 8, l ^ 16, l ^ 32 share the
         // channel block), then the 8 waves, in a fixed order
 #pragma unroll
@@ -658,6 +665,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         }
         lds_barrier();   // `red` and `gsum` are rewritten by the next tile
     }
+    tl_mark(a.tl, 0, 3);
 }
 
 template <int KIND, int PX>
@@ -684,8 +692,8 @@ static hipError_t stage1_px(const Stage1Args& a, int B, hipStream_t s) {
 hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyView& p, float* key,
                          double* part, unsigned long long* tcnt, uint32_t gen,
                          const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
-                         hipStream_t s) {
-    Stage1Args a{x, d, k_in, p, key, part, tcnt, h_tap, key_tap, in_idx_tap, g.tiles, g.nch, g.nb1, gen};
+                         unsigned long long* tl, hipStream_t s) {
+    Stage1Args a{x, d, k_in, p, key, part, tcnt, h_tap, key_tap, in_idx_tap, g.tiles, g.nch, g.nb1, gen, tl};
     return p.kind == 1 ? stage1_px<1>(a, B, s) : stage1_px<2>(a, B, s);
 }
 
@@ -712,6 +720,7 @@ struct Stage2Args {
     uint8_t* mask;        // [B][F] or null
     float* ypart;         // [B][W2][d]
     int32_t* stream_tap;  // [B][k] or null: the channels the blocks stream, by share
+    unsigned long long* tl;   // timeline stamps or null
 };
 
 constexpr int kS2Threads = 512;
@@ -850,6 +859,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     __shared__ int wc[4][NW];
     __shared__ float red[2][NW * 2 * G];
 
+    tl_mark(a.tl, 1, 0);
     const int w = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int F = a.F, k = a.k, W2 = a.W2;
     const int r0 = (int)((long long)w * F / W2), r1 = (int)((long long)(w + 1) * F / W2);
@@ -1149,6 +1159,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     // on any path that merges pending and completed loads the compiler drains
     // every load and the overlap is lost.  After the last group, `cur` is
     // loaded past the list (zeros, no memory access) and left unused.
+    tl_mark(a.tl, 1, 1);
     const int rest = n - E;
     const int groups = 1 + (rest + G - 1) / G;
     float xr[R][8];
@@ -1185,6 +1196,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     }
     if (gi < groups) consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
     if (groups < 2) write_range();
+    tl_mark(a.tl, 1, 2);
     float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1194,6 +1206,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             *reinterpret_cast<float4*>(dst + col + 4) = make_float4(yacc[r][4], yacc[r][5], yacc[r][6], yacc[r][7]);
         }
     }
+    tl_mark(a.tl, 1, 3);
 }
 
 template <int PK, int R, int G, bool STREAM>
@@ -1228,8 +1241,8 @@ static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
 hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
                          const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
                          int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, int32_t* stream_tap,
-                         hipStream_t s) {
-    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart, stream_tap};
+                         unsigned long long* tl, hipStream_t s) {
+    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart, stream_tap, tl};
     // channels per group: the fewest that keep the stream at its rate (more
     // rows in flight per block measured slower on the 4096 and 8192 shapes)
     if (d <= 4096) return stage2_pk<1, 2, true>(a, B, s);
@@ -1239,7 +1252,7 @@ hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t
 
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
                          int32_t* idx, uint8_t* mask, hipStream_t s) {
-    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr, nullptr};
+    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr, nullptr, nullptr};
     return stage2_pk<1, 1, false>(a, B, s);
 }
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PROX_ABI_VERSION 2
+#define PROX_ABI_VERSION 3
 
 typedef enum {
     PROX_OK = 0,
@@ -123,7 +123,12 @@ typedef struct {
  *   stream_idx [batch][k_ff]  below 4 tokens per call only (untouched from 4):
  *          the channels whose rows the Stage-2 blocks actually stream, each
  *          block's list at the ranks of its share; over all blocks a
- *          permutation of idx when no channel is lost or streamed twice.     */
+ *          permutation of idx when no channel is lost or streamed twice.
+ *   timeline [2][1024][8]  below 4 tokens per call only: the GPU's 100 MHz
+ *          real-time counter, stored by each block of Stage 1 (index 0) and
+ *          Stage 2 (index 1; block = token * blocks per token + block) at
+ *          points 0 start, 1 selection done, 2 stream done (Stage 1: of its
+ *          last tile), 3 end; points 4-7 unused.                              */
 typedef struct {
     int32_t* in_idx;
     float* key;
@@ -132,6 +137,7 @@ typedef struct {
     int32_t n_events;
     int32_t reserved;
     int32_t* stream_idx;
+    uint64_t* timeline;
 } prox_taps;
 
 /* ABI version compiled into the library (PROX_ABI_VERSION). */
