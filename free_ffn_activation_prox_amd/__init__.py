@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprox_hip.so")
 
 PROX_OK = 0
-KINDS = {"int8": 1, "int4": 2}
+KINDS = {"int8": 1, "int4": 2, "exact": 3}
 
 
 class ProxError(RuntimeError):
@@ -77,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "prox_ffn_forward_noalloc": (I32, [P, I32, ctypes.POINTER(_Weights), ctypes.POINTER(_Proxy), I32, I32,
                                            P, P, P, P]),
         "prox_read_probe": (I32, [P, SZ, P, I32, P]),
+        "prox_quality": (I32, [P, P, I32, I32, P, P, I32, P, P, P]),
         "prox_status_str": (ctypes.c_char_p, [I32]),
         "prox_last_error": (ctypes.c_char_p, []),
     }
@@ -167,8 +168,14 @@ class Proxy:
 
 
 def build_proxy(weights: Weights, kind: str, stream=None) -> Proxy:
-    """Quantized proxy of W_gate / W_up (one-time, training-free)."""
+    """Quantized proxy of W_gate / W_up (one-time, training-free).  kind
+    "exact" (exact-mask mode) builds nothing: the weights rank themselves."""
     import torch
+    if kind == "exact":
+        desc = _Proxy()
+        _check(_lib.prox_build_proxy(ctypes.byref(weights._c), KINDS[kind], None, 0, ctypes.byref(desc),
+                                     _stream_ptr(stream)), "prox_build_proxy")
+        return Proxy(kind, None, desc)
     nbytes = proxy_bytes(weights.d_model, weights.d_ff, kind)
     if nbytes == 0:
         raise ValueError("invalid shape/kind for a proxy")
@@ -269,6 +276,23 @@ def timeline_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *,
     return tl.view(2, 1024, 8)
 
 
+def quality(mask_a, mask_b, y, y_ref, stream=None):
+    """Quality diagnostics (prox_quality) on device tensors: per token, the kept
+    channels two masks share (uint8 [B][F] each) and ||y - y_ref|| / ||y_ref||
+    (fp32 [B][d] each).  Returns (overlap int32 [B], err float64 [B])."""
+    import torch
+    B, F = mask_a.shape
+    d = y.shape[1]
+    for t, dt in ((mask_a, torch.uint8), (mask_b, torch.uint8), (y, torch.float32), (y_ref, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous() or t.shape[0] != B:
+            raise ValueError("quality: wrong dtype, layout or batch")
+    overlap = torch.empty(B, dtype=torch.int32, device=y.device)
+    err = torch.empty(B, dtype=torch.float64, device=y.device)
+    _check(_lib.prox_quality(mask_a.data_ptr(), mask_b.data_ptr(), B, F, y.data_ptr(), y_ref.data_ptr(), d,
+                             overlap.data_ptr(), err.data_ptr(), _stream_ptr(stream)), "prox_quality")
+    return overlap, err
+
+
 def noalloc_scratch_bytes() -> int:
     return _lib.prox_noalloc_scratch_bytes()
 
@@ -295,5 +319,5 @@ def ffn_forward_noalloc(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int,
     return y, mask, idx[:, :k_ff]
 
 
-__all__ = ["timeline_forward", "read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
+__all__ = ["quality", "timeline_forward", "read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
            "build_proxy", "alloc_workspace", "ffn_forward", "LIB_PATH", "KINDS", "N_PHASES", "PHASES"]

@@ -32,7 +32,9 @@ prox_status hip_fail(hipError_t e, const char* where) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-bool kind_ok(int kind) { return kind == PROX_PROXY_INT8 || kind == PROX_PROXY_INT4_G128; }
+bool kind_ok(int kind) {
+    return kind == PROX_PROXY_INT8 || kind == PROX_PROXY_INT4_G128 || kind == PROX_PROXY_EXACT_BF16;
+}
 
 const char* shape_error(int d, int F, int kind) {
     if (!kind_ok(kind)) return "unknown proxy kind";
@@ -57,6 +59,11 @@ ProxyGeom proxy_geom(int d, int F, int kind) {
     ProxyGeom g;
     g.tile_ch = tile_channels(kind);
     g.f_pad = f_pad_of(F, kind);
+    if (kind == PROX_PROXY_EXACT_BF16) {      // no proxy: the weights rank themselves
+        g.groups = 0;
+        g.row_stride = g.scale_offset = g.bytes = 0;
+        return g;
+    }
     g.groups = kind == PROX_PROXY_INT8 ? 1 : d / kInt4Group;
     g.row_stride = kTileRowBytes;
     const size_t codes = (size_t)(g.f_pad / g.tile_ch) * d * kTileRowBytes;
@@ -115,7 +122,8 @@ extern "C" size_t prox_workspace_bytes(int32_t d, int32_t F, int32_t batch, int3
 extern "C" prox_status prox_build_proxy(const prox_weights* w, int32_t kind, void* buf,
                                         size_t buf_bytes, prox_proxy* out, void* stream) {
     g_err.clear();
-    if (!w || !out || !buf) return fail(PROX_E_INVALID, "null weights, output descriptor or buffer");
+    if (!w || !out) return fail(PROX_E_INVALID, "null weights or output descriptor");
+    if (!buf && kind != PROX_PROXY_EXACT_BF16) return fail(PROX_E_INVALID, "null proxy buffer");
     if (!w->w_gate_t || !w->w_up_t) return fail(PROX_E_INVALID, "null w_gate_t or w_up_t");
     if (const char* e = shape_error(w->d_model, w->d_ff, kind)) return fail(PROX_E_INVALID, "%s", e);
     if (const char* e = limit_error(w->d_model, w->d_ff)) return fail(PROX_E_UNSUPPORTED, "%s", e);
@@ -136,6 +144,10 @@ extern "C" prox_status prox_build_proxy(const prox_weights* w, int32_t kind, voi
     p.scale_offset = g.scale_offset;
     p.bytes = g.bytes;
     p.buf = buf;
+    if (kind == PROX_PROXY_EXACT_BF16) {      // nothing to build
+        *out = p;
+        return PROX_OK;
+    }
     hipError_t e = launch_build_proxy(static_cast<const uint16_t*>(w->w_gate_t),
                                       static_cast<const uint16_t*>(w->w_up_t), w->d_model,
                                       w->d_ff, view_of(&p), (hipStream_t)stream);
@@ -152,8 +164,8 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     g_err.clear();
     if (!x || !w || !p || !y || !workspace)
         return fail(PROX_E_INVALID, "null x, weights, proxy, y or workspace");
-    if (!w->w_gate_t || !w->w_up_t || !w->w_down || !p->buf)
-        return fail(PROX_E_INVALID, "null weight or proxy buffer");
+    if (!w->w_gate_t || !w->w_up_t || !w->w_down) return fail(PROX_E_INVALID, "null weight buffer");
+    if (!p->buf && p->kind != PROX_PROXY_EXACT_BF16) return fail(PROX_E_INVALID, "null proxy buffer");
     const int d = w->d_model, F = w->d_ff;
     if (const char* e = shape_error(d, F, p->kind)) return fail(PROX_E_INVALID, "%s", e);
     if (const char* e = limit_error(d, F)) return fail(PROX_E_UNSUPPORTED, "%s", e);
@@ -161,13 +173,15 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     if (batch > PROX_MAX_BATCH) return fail(PROX_E_UNSUPPORTED, "batch above PROX_MAX_BATCH");
     if (k_in < 0 || k_in > d) return fail(PROX_E_INVALID, "k_in out of [0, d_model]");
     if (k_ff < 0 || k_ff > F) return fail(PROX_E_INVALID, "k_ff out of [0, d_ff]");
+    if (p->kind == PROX_PROXY_EXACT_BF16 && k_in != d)
+        return fail(PROX_E_INVALID, "exact mode keeps every input: k_in must equal d_model");
     if (p->d_model != d || p->d_ff != F) return fail(PROX_E_MISMATCH, "proxy shape differs from weights");
     const ProxyGeom g = proxy_geom(d, F, p->kind);
     if (p->f_pad != g.f_pad || p->groups != g.groups || p->tile_ch != g.tile_ch || p->row_stride != g.row_stride ||
         p->scale_offset != g.scale_offset || p->bytes != g.bytes)
         return fail(PROX_E_MISMATCH, "proxy descriptor is not the one prox_build_proxy writes");
     if (!aligned(x, 16) || !aligned(w->w_gate_t, 16) || !aligned(w->w_up_t, 16) ||
-        !aligned(w->w_down, 16) || !aligned(y, 16) || !aligned(p->buf, 256))
+        !aligned(w->w_down, 16) || !aligned(y, 16) || (p->kind != PROX_PROXY_EXACT_BF16 && !aligned(p->buf, 256)))
         return fail(PROX_E_INVALID, "misaligned x, weights, y or proxy");
     if (!aligned(workspace, 256)) return fail(PROX_E_INVALID, "workspace must be 256-byte aligned");
     const WsLayout L = ws_layout(d, F, batch, p->kind);
@@ -197,6 +211,28 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     const uint16_t* wg = static_cast<const uint16_t*>(w->w_gate_t);
     const uint16_t* wu = static_cast<const uint16_t*>(w->w_up_t);
     const uint16_t* wd = static_cast<const uint16_t*>(w->w_down);
+
+    if (p->kind == PROX_PROXY_EXACT_BF16) {
+        // exact mode: h of every channel (fp64), then the selection and the
+        // W_down rows of the kept channels with h read back; per-token
+        // kernels for any batch
+        double* hx = reinterpret_cast<double*>(ws + L.hx);
+        const int nb = n_cu / batch > 0 ? n_cu / batch : 1;
+        const int W2x = stage2_blocks(batch, k_ff, d <= 4096 ? n_cu : n_cu * 3 / 4);
+        unsigned long long* tl = taps ? (unsigned long long*)taps->timeline : nullptr;
+        e = launch_exact_h(xb, batch, d, wg, wu, F, g.f_pad, nb, key, hx, taps ? taps->h_hat : nullptr,
+                           taps ? taps->key : nullptr, taps ? taps->in_idx : nullptr, tl, s);
+        if (e != hipSuccess) return hip_fail(e, "exact stage 1");
+        if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
+        e = launch_stage2(xb, wg, wu, wd, key, batch, d, F, g.f_pad, k_ff, W2x, idx, mask, ypart,
+                          taps ? taps->stream_idx : nullptr, tl, 2, hx, nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "exact stage 2");
+        if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
+        e = launch_reduce_y(ypart, batch, d, W2x, y, s);
+        if (e != hipSuccess) return hip_fail(e, "reduce y");
+        if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
+        return PROX_OK;
+    }
 
     if (batch >= kBatchMin) {
         // matrix-core path: input selection and proxy GEMM over the batch,
@@ -230,7 +266,8 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     if (e != hipSuccess) return hip_fail(e, "stage 1");
     if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_stage2(xb, wg, wu, wd, key, batch, d, F, g.f_pad, k_ff, W2, idx, mask, ypart,
-                      taps ? taps->stream_idx : nullptr, taps ? (unsigned long long*)taps->timeline : nullptr, s);
+                      taps ? taps->stream_idx : nullptr, taps ? (unsigned long long*)taps->timeline : nullptr, 1,
+                      nullptr, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "stage 2");
     if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
     e = launch_reduce_y(ypart, batch, d, W2, y, s);
@@ -305,6 +342,21 @@ extern "C" prox_status prox_ffn_forward_noalloc(const void* x, int32_t batch, co
     if (!ws) return st;
     // need == 0 (invalid shape or batch): prox_ffn_forward_taps reports it
     return prox_ffn_forward_taps(x, batch, w, p, k_in, k_ff, y, mask, idx, ws, kScratchBytes, nullptr, stream);
+}
+
+extern "C" prox_status prox_quality(const uint8_t* mask_a, const uint8_t* mask_b, int32_t batch, int32_t d_ff,
+                                    const float* y, const float* y_ref, int32_t d_model, int32_t* overlap,
+                                    double* err, void* stream) {
+    g_err.clear();
+    if (batch < 1 || d_ff < 1 || d_model < 1) return fail(PROX_E_INVALID, "batch, d_ff and d_model must be >= 1");
+    if ((!mask_a) != (!mask_b) || (!mask_a) != (!overlap))
+        return fail(PROX_E_INVALID, "mask_a, mask_b and overlap must all be given or all be null");
+    if ((!y) != (!y_ref) || (!y) != (!err))
+        return fail(PROX_E_INVALID, "y, y_ref and err must all be given or all be null");
+    if (!mask_a && !y) return fail(PROX_E_INVALID, "nothing to compare");
+    hipError_t e = launch_quality(mask_a, mask_b, batch, d_ff, y, y_ref, d_model, overlap, err, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quality");
+    return PROX_OK;
 }
 
 extern "C" const char* prox_status_str(int32_t st) {

@@ -25,7 +25,9 @@ inline __host__ __device__ int s2_keys_words(int F) {
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline int tile_channels(int kind) { return kind == 1 ? 64 : 128; }
+// channels per proxy tile: int8 64, int4 128; exact mode (kind 3) has no
+// proxy and pads the keys to 64 channels
+inline int tile_channels(int kind) { return kind == 2 ? 128 : 64; }
 inline int f_pad_of(int F, int kind) { return (int)align_up((size_t)F, (size_t)tile_channels(kind)); }
 
 struct ProxyView {
@@ -102,11 +104,11 @@ DnSplit down_batch_split(int B, int d, int F);
 // Workspace carve-up (byte offsets) for one (d, F, B, kind).  The batch
 // regions (xm, bpart, bmask, hb) are empty below kBatchMin tokens.
 struct WsLayout {
-    size_t key, ypart, part, tcnt, xm, bpart, bmask, hb, total;
+    size_t key, ypart, part, tcnt, xm, bpart, bmask, hb, hx, total;
 };
 inline WsLayout ws_layout(int d, int F, int B, int kind) {
     const int fp = f_pad_of(F, kind);
-    const bool batch = B >= kBatchMin;
+    const bool batch = B >= kBatchMin && kind != 3;   // exact mode runs the per-token kernels
     const size_t ks1 = batch ? (size_t)proxy_batch_split(d, F, kind).ks1 : 0;
     WsLayout L;
     size_t o = 0;
@@ -118,6 +120,7 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
     L.bpart = o;  o = align_up(o + (ks1 > 1 ? ks1 * 2 * B * fp * 4 : 0), 256);
     L.bmask = o;  o = align_up(o + (batch ? (size_t)B * F : 0), 256);
     L.hb = o;     o = align_up(o + (batch ? (size_t)2 * B * fp * 2 : 0), 256);
+    L.hx = o;     o = align_up(o + (kind == 3 ? (size_t)B * F * 8 : 0), 256);
     L.total = o;
     return L;
 }
@@ -129,14 +132,23 @@ hipError_t launch_stage1(const uint16_t* x, int B, int d, int k_in, const ProxyV
                          double* part, unsigned long long* tcnt, uint32_t gen,
                          const S1Geom& g, double* h_tap, float* key_tap, int32_t* in_idx_tap,
                          unsigned long long* tl, hipStream_t s);
-hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
-                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
-                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, int32_t* stream_tap,
-                         unsigned long long* tl, hipStream_t s);
+// Stage 2 stream modes: 1 bf16 rows, 2 exact mode (h from hsrc [B][F], down
+// rows only), 3 int8 rows (codes [F][d] each, qscale [3][F]).
+hipError_t launch_stage2(const uint16_t* x, const void* wg_t, const void* wu_t, const void* wd, const float* key,
+                         int B, int d, int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart,
+                         int32_t* stream_tap, unsigned long long* tl, int mode, const double* hsrc,
+                         const float* qscale, hipStream_t s);
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s);
 // Stage-2 selection only: mask (required) and idx (nullable) from the keys.
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
                          int32_t* idx, uint8_t* mask, hipStream_t s);
+
+// ---- exact mode and diagnostics (prox_exact.hip)
+hipError_t launch_exact_h(const uint16_t* x, int B, int d, const uint16_t* wg_t, const uint16_t* wu_t, int F,
+                          int f_pad, int nb, float* key, double* hbuf, double* h_tap, float* key_tap,
+                          int32_t* in_idx_tap, unsigned long long* tl, hipStream_t s);
+hipError_t launch_quality(const uint8_t* ma, const uint8_t* mb, int B, int F, const float* y, const float* yr, int d,
+                          int32_t* overlap, double* err, hipStream_t s);
 
 // ---- batch launchers (prox_batch.hip)
 hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,

@@ -721,14 +721,32 @@ struct Stage2Args {
     float* ypart;         // [B][W2][d]
     int32_t* stream_tap;  // [B][k] or null: the channels the blocks stream, by share
     unsigned long long* tl;   // timeline stamps or null
+    const double* hsrc;   // mode 2: exact h [B][F]
+    const float* qscale;  // mode 3: row scales [3][F] (gate, up, down)
 };
 
 constexpr int kS2Threads = 512;
 
-// Thread t covers columns r * 4096 + 8t .. +8 (r < R) of every row.
-template <int R, int G>
+// Thread t covers columns r * 4096 + 8t .. +8 (r < R) of every row.  The rows a
+// group holds, by stream mode:
+//   1  bf16 gate, up and down rows (h computed here);
+//   2  bf16 down rows; h of each channel read from memory (exact mode, where
+//      Stage 1 computed the exact h of every channel);
+//   3  int8 gate, up and down rows (8 bytes per thread per part) and the
+//      rows' fp32 scales (quantized Stage-2 weights).
+template <int MODE, int R, int G>
 struct RowGroup {
     uint4 g[G][R], u[G][R], dn[G][R];
+};
+template <int R, int G>
+struct RowGroup<2, R, G> {
+    uint4 dn[G][R];
+    float h[G];
+};
+template <int R, int G>
+struct RowGroup<3, R, G> {
+    uint2 g[G][R], u[G][R], dn[G][R];
+    float sg[G], su[G], sd[G];
 };
 
 // Rows of list entries v0 .. v0 + G - 1 (buffer loads: the row offset is
@@ -739,21 +757,49 @@ struct RowGroup {
 struct RowRsrc {
     __amdgpu_buffer_rsrc_t g, u, dn;
 };
+// Per-channel values the stream modes read from memory: h (mode 2, this
+// token's [F]) or the rows' scales (mode 3, [F] each).
+struct RowAux {
+    const double* h;
+    const float* sg;
+    const float* su;
+    const float* sd;
+};
 
-template <int R, int G>
-__device__ __forceinline__ void load_group(const RowRsrc& rs, const uint16_t* chan, int v0, int cnt,
-                                           uint32_t row_bytes, uint32_t oob, const uint32_t (&voff)[R],
-                                           RowGroup<R, G>& rg) {
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    return make_uint2(v.x, v.y);
+}
+
+template <int MODE, int R, int G>
+__device__ __forceinline__ void load_group(const RowRsrc& rs, const RowAux& aux, const uint16_t* chan, int v0,
+                                           int cnt, uint32_t row_bytes, uint32_t oob, const uint32_t (&voff)[R],
+                                           RowGroup<MODE, R, G>& rg) {
 #pragma unroll
     for (int q = 0; q < G; ++q) {
         const bool ok = v0 + q < cnt;
-        const uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)chan[min(v0 + q, max(cnt - 1, 0))]) * row_bytes;
+        const int j = __builtin_amdgcn_readfirstlane((int)chan[min(v0 + q, max(cnt - 1, 0))]);
+        const uint32_t soff = (uint32_t)j * row_bytes;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t vo = ok ? voff[r] : oob;
-            rg.g[q][r] = buf_load16(rs.g, vo, soff);
-            rg.u[q][r] = buf_load16(rs.u, vo, soff);
-            rg.dn[q][r] = buf_load16(rs.dn, vo, soff);
+            if constexpr (MODE == 1) {
+                rg.g[q][r] = buf_load16(rs.g, vo, soff);
+                rg.u[q][r] = buf_load16(rs.u, vo, soff);
+                rg.dn[q][r] = buf_load16(rs.dn, vo, soff);
+            } else if constexpr (MODE == 2) {
+                rg.dn[q][r] = buf_load16(rs.dn, vo, soff);
+            } else {
+                rg.g[q][r] = buf_load8(rs.g, vo, soff);
+                rg.u[q][r] = buf_load8(rs.u, vo, soff);
+                rg.dn[q][r] = buf_load8(rs.dn, vo, soff);
+            }
+        }
+        if constexpr (MODE == 2) rg.h[q] = (float)aux.h[j];
+        if constexpr (MODE == 3) {
+            rg.sg[q] = aux.sg[j];
+            rg.su[q] = aux.su[j];
+            rg.sd[q] = aux.sd[j];
         }
     }
 }
@@ -783,49 +829,89 @@ __device__ __forceinline__ void axpy8(float h, uint4 v, float (&y)[8]) {
     y[6] = fmaf(h, bf16_lo(v.w), y[6]); y[7] = fmaf(h, bf16_hi(v.w), y[7]);
 }
 
+__device__ __forceinline__ float dot8_i8(const float (&x)[8], uint2 v, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(x[e], (float)sext8(v.x, e), acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(x[4 + e], (float)sext8(v.y, e), acc);
+    return acc;
+}
+
+__device__ __forceinline__ void axpy8_i8(float h, uint2 v, float (&y)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = fmaf(h, (float)sext8(v.x, e), y[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[4 + e] = fmaf(h, (float)sext8(v.y, e), y[4 + e]);
+}
+
 // Gate/up dots of a group (fp32), reduced over the block's waves through LDS
 // (`red` = this parity's [wave][2G] buffer), then h = silu(g) u for the
-// `nvalid` leading entries and the W_down rows accumulated into y.
-template <int R, int G>
-__device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const float (&xr)[R][8],
+// `nvalid` leading entries and the W_down rows accumulated into y.  Mode 2
+// takes h as read; mode 3 scales the integer-code dots by the rows' scales
+// (g = s_g x.q_g, u = s_u x.q_u, and the down row s_d q_d).
+template <int MODE, int R, int G>
+__device__ __forceinline__ void consume_group(const RowGroup<MODE, R, G>& rg, const float (&xr)[R][8],
                                               float (&yacc)[R][8], int nvalid, float* red) {
     constexpr int NW = kS2Threads / kWave;
-    const int t = threadIdx.x, w = t >> 6, l = t & 63;
-    float pg[G], pu[G];
+    float h[G];
+    if constexpr (MODE == 2) {
 #pragma unroll
-    for (int q = 0; q < G; ++q) {
-        float ga = 0.f, ua = 0.f;
+        for (int q = 0; q < G; ++q) h[q] = q < nvalid ? rg.h[q] : 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            ga = dot8(xr[r], rg.g[q][r], ga);
-            ua = dot8(xr[r], rg.u[q][r], ua);
-        }
-        pg[q] = wave_sum(ga);
-        pu[q] = wave_sum(ua);
-    }
-    if (l == 0) {
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int r = 0; r < R; ++r) axpy8(h[q], rg.dn[q][r], yacc[r]);
+        return;
+    } else {
+        const int t = threadIdx.x, w = t >> 6, l = t & 63;
+        float pg[G], pu[G];
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-            red[w * 2 * G + 2 * q] = pg[q];
-            red[w * 2 * G + 2 * q + 1] = pu[q];
+            float ga = 0.f, ua = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if constexpr (MODE == 1) {
+                    ga = dot8(xr[r], rg.g[q][r], ga);
+                    ua = dot8(xr[r], rg.u[q][r], ua);
+                } else {
+                    ga = dot8_i8(xr[r], rg.g[q][r], ga);
+                    ua = dot8_i8(xr[r], rg.u[q][r], ua);
+                }
+            }
+            pg[q] = wave_sum(ga);
+            pu[q] = wave_sum(ua);
+        }
+        if (l == 0) {
+#pragma unroll
+            for (int q = 0; q < G; ++q) {
+                red[w * 2 * G + 2 * q] = pg[q];
+                red[w * 2 * G + 2 * q + 1] = pu[q];
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                gs += red[v * 2 * G + 2 * q];
+                us += red[v * 2 * G + 2 * q + 1];
+            }
+            if constexpr (MODE == 3) {
+                gs *= rg.sg[q];
+                us *= rg.su[q];
+            }
+            h[q] = q < nvalid ? gs / (1.f + expf(-gs)) * us : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if constexpr (MODE == 1) axpy8(h[q], rg.dn[q][r], yacc[r]);
+                else axpy8_i8(h[q] * rg.sd[q], rg.dn[q][r], yacc[r]);
+            }
         }
     }
-    lds_barrier();
-    float h[G];
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-        float gs = 0.f, us = 0.f;
-#pragma unroll
-        for (int v = 0; v < NW; ++v) {
-            gs += red[v * 2 * G + 2 * q];
-            us += red[v * 2 * G + 2 * q + 1];
-        }
-        h[q] = q < nvalid ? gs / (1.f + expf(-gs)) * us : 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < G; ++q)
-#pragma unroll
-        for (int r = 0; r < R; ++r) axpy8(h[q], rg.dn[q][r], yacc[r]);
 }
 
 // ---------------------------------------------------------------------------
@@ -848,8 +934,10 @@ __device__ __forceinline__ void consume_group(const RowGroup<R, G>& rg, const fl
 constexpr int kSmallCand = 128;   // candidates ranked by direct comparison up to this many
 constexpr int kCandCap = 1024;    // candidates listed in LDS (more: the slow path)
 
-template <int PK, int R, int G, bool STREAM>
+template <int PK, int R, int G, int MODE>
 __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
+    constexpr bool STREAM = MODE != 0;       // 0: selection only (mask and idx)
+    constexpr int SM = STREAM ? MODE : 1;    // the stream code's mode (unused when MODE == 0)
     constexpr int NT = kS2Threads;
     constexpr int NW = NT / kWave;
     extern __shared__ uint4 dyn2v[];                     // 16-byte aligned
@@ -871,16 +959,19 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     uint16_t* chan = kr + kCandCap;                        // [cap + 64] the block's list
     const float* keyb = a.key + (size_t)b * a.f_pad;
 
-    const uint32_t row_bytes = (uint32_t)a.d * 2u;
+    constexpr uint32_t EB = MODE == 3 ? 1u : 2u;          // bytes per weight
+    const uint32_t row_bytes = (uint32_t)a.d * EB;
     const uint32_t mat_bytes = (uint32_t)F * row_bytes;
     const RowRsrc rs{make_rsrc(a.wg_t, mat_bytes), make_rsrc(a.wu_t, mat_bytes), make_rsrc(a.wd, mat_bytes)};
+    const RowAux aux{a.hsrc ? a.hsrc + (size_t)b * F : nullptr, a.qscale, a.qscale ? a.qscale + F : nullptr,
+                     a.qscale ? a.qscale + 2 * (size_t)F : nullptr};
     uint32_t voff[R];
     uint4 xv[R];                    // this thread's 8 x values per row part, as loaded (converted
     float yacc[R][8];               // when the stream starts: nothing before it waits for them)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int col = r * 4096 + t * 8;
-        voff[r] = col < a.d ? (uint32_t)col * 2u : mat_bytes;   // past d: read as zeros
+        voff[r] = col < a.d ? (uint32_t)col * EB : mat_bytes;   // past d: read as zeros
         xv[r] = make_uint4(0, 0, 0, 0);
         if (STREAM && col < a.d) xv[r] = *reinterpret_cast<const uint4*>(a.x + (size_t)b * a.d + col);
 #pragma unroll
@@ -1004,8 +1095,8 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int cs = sc[16];                                 // candidates before the range
     const int cert_before = sc[18];                        // certain keys before the range
     const int E = min(nc, G);
-    RowGroup<R, G> cur, nxt;
-    if constexpr (STREAM) load_group<R, G>(rs, chan, 0, E, row_bytes, mat_bytes, voff, cur);
+    RowGroup<SM, R, G> cur, nxt;
+    if constexpr (STREAM) load_group<SM, R, G>(rs, aux, chan, 0, E, row_bytes, mat_bytes, voff, cur);
 
     int nks = 0, kc_before = 0, s0k = 0;
     if (listed) {
@@ -1174,27 +1265,27 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     if (groups >= 2) {
         // the first two groups: the mask and idx of the block's range are
         // written while both are in flight
-        load_group<R, G>(rs, chan, E, n, row_bytes, mat_bytes, voff, nxt);
+        load_group<SM, R, G>(rs, aux, chan, E, n, row_bytes, mat_bytes, voff, nxt);
         write_range();
-        consume_group<R, G>(cur, xr, yacc, E, red[0]);
+        consume_group<SM, R, G>(cur, xr, yacc, E, red[0]);
         settle(yacc);
-        load_group<R, G>(rs, chan, E + G, n, row_bytes, mat_bytes, voff, cur);
-        consume_group<R, G>(nxt, xr, yacc, min(G, rest), red[1]);
+        load_group<SM, R, G>(rs, aux, chan, E + G, n, row_bytes, mat_bytes, voff, cur);
+        consume_group<SM, R, G>(nxt, xr, yacc, min(G, rest), red[1]);
         settle(yacc);
         gi = 2;
     }
     for (; gi + 1 < groups; gi += 2) {
-        load_group<R, G>(rs, chan, E + gi * G, n, row_bytes, mat_bytes, voff, nxt);
-        consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
+        load_group<SM, R, G>(rs, aux, chan, E + gi * G, n, row_bytes, mat_bytes, voff, nxt);
+        consume_group<SM, R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
         // The accumulation into y must finish before `cur` is reloaded: if the
         // compiler sinks it below the reloads, the old and new `cur` overlap
         // and the loop-carried registers need a copy that waits for the loads.
         settle(yacc);
-        load_group<R, G>(rs, chan, E + (gi + 1) * G, n, row_bytes, mat_bytes, voff, cur);
-        consume_group<R, G>(nxt, xr, yacc, min(G, rest - gi * G), red[1]);
+        load_group<SM, R, G>(rs, aux, chan, E + (gi + 1) * G, n, row_bytes, mat_bytes, voff, cur);
+        consume_group<SM, R, G>(nxt, xr, yacc, min(G, rest - gi * G), red[1]);
         settle(yacc);
     }
-    if (gi < groups) consume_group<R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
+    if (gi < groups) consume_group<SM, R, G>(cur, xr, yacc, gi == 0 ? E : min(G, rest - (gi - 1) * G), red[0]);
     if (groups < 2) write_range();
     tl_mark(a.tl, 1, 2);
     float* dst = a.ypart + ((size_t)b * W2 + w) * a.d;
@@ -1209,13 +1300,13 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     tl_mark(a.tl, 1, 3);
 }
 
-template <int PK, int R, int G, bool STREAM>
+template <int PK, int R, int G, int MODE>
 static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     // list length bound: ceil(C/W2) + ceil(KC/W2); selection only keeps no list
-    const int cap = STREAM ? (a.k + a.W2 - 1) / a.W2 + 2 : 0;
+    const int cap = MODE != 0 ? (a.k + a.W2 - 1) / a.W2 + 2 : 0;
     const size_t dyn = (size_t)s2_keys_words(a.F) * 4 + ((size_t)kCandCap + 64) * 4 +
                        ((size_t)kCandCap * 2 + 64 + cap + 64) * 2;
-    auto fn = k_stage2<PK, R, G, STREAM>;
+    auto fn = k_stage2<PK, R, G, MODE>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
@@ -1224,36 +1315,50 @@ static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int R, int G, bool STREAM>
+template <int R, int G, int MODE>
 static hipError_t stage2_pk(const Stage2Args& a, int B, hipStream_t s) {
     const int per = (a.F + kS2Threads - 1) / kS2Threads;
-    if (per <= 4) return go_stage2<4, R, G, STREAM>(a, B, s);
-    if (per <= 8) return go_stage2<8, R, G, STREAM>(a, B, s);
-    if (per <= 16) return go_stage2<16, R, G, STREAM>(a, B, s);
-    if (per <= 24) return go_stage2<24, R, G, STREAM>(a, B, s);
-    if (per <= 32) return go_stage2<32, R, G, STREAM>(a, B, s);
-    if (per <= 40) return go_stage2<40, R, G, STREAM>(a, B, s);
-    if (per <= 48) return go_stage2<48, R, G, STREAM>(a, B, s);
-    if (per <= 56) return go_stage2<56, R, G, STREAM>(a, B, s);
-    return go_stage2<64, R, G, STREAM>(a, B, s);
+    if (per <= 4) return go_stage2<4, R, G, MODE>(a, B, s);
+    if (per <= 8) return go_stage2<8, R, G, MODE>(a, B, s);
+    if (per <= 16) return go_stage2<16, R, G, MODE>(a, B, s);
+    if (per <= 24) return go_stage2<24, R, G, MODE>(a, B, s);
+    if (per <= 32) return go_stage2<32, R, G, MODE>(a, B, s);
+    if (per <= 40) return go_stage2<40, R, G, MODE>(a, B, s);
+    if (per <= 48) return go_stage2<48, R, G, MODE>(a, B, s);
+    if (per <= 56) return go_stage2<56, R, G, MODE>(a, B, s);
+    return go_stage2<64, R, G, MODE>(a, B, s);
 }
 
-hipError_t launch_stage2(const uint16_t* x, const uint16_t* wg_t, const uint16_t* wu_t,
-                         const uint16_t* wd, const float* key, int B, int d, int F, int f_pad,
-                         int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart, int32_t* stream_tap,
-                         unsigned long long* tl, hipStream_t s) {
-    Stage2Args a{x, wg_t, wu_t, wd, key, d, F, f_pad, k_ff, W2, idx, mask, ypart, stream_tap, tl};
+hipError_t launch_stage2(const uint16_t* x, const void* wg_t, const void* wu_t, const void* wd, const float* key,
+                         int B, int d, int F, int f_pad, int k_ff, int W2, int32_t* idx, uint8_t* mask, float* ypart,
+                         int32_t* stream_tap, unsigned long long* tl, int mode, const double* hsrc,
+                         const float* qscale, hipStream_t s) {
+    Stage2Args a{x, static_cast<const uint16_t*>(wg_t), static_cast<const uint16_t*>(wu_t),
+                 static_cast<const uint16_t*>(wd), key, d, F, f_pad, k_ff, W2, idx, mask, ypart, stream_tap, tl,
+                 hsrc, qscale};
     // channels per group: the fewest that keep the stream at its rate (more
     // rows in flight per block measured slower on the 4096 and 8192 shapes)
-    if (d <= 4096) return stage2_pk<1, 2, true>(a, B, s);
-    if (d <= 8192) return stage2_pk<2, 1, true>(a, B, s);
-    return stage2_pk<4, 1, true>(a, B, s);
+    if (mode == 2) {
+        // exact mode streams one row per channel: more channels per group
+        if (d <= 4096) return stage2_pk<1, 4, 2>(a, B, s);
+        if (d <= 8192) return stage2_pk<2, 2, 2>(a, B, s);
+        return stage2_pk<4, 1, 2>(a, B, s);
+    }
+    if (mode == 3) {
+        if (d <= 4096) return stage2_pk<1, 2, 3>(a, B, s);
+        if (d <= 8192) return stage2_pk<2, 1, 3>(a, B, s);
+        return stage2_pk<4, 1, 3>(a, B, s);
+    }
+    if (d <= 4096) return stage2_pk<1, 2, 1>(a, B, s);
+    if (d <= 8192) return stage2_pk<2, 1, 1>(a, B, s);
+    return stage2_pk<4, 1, 1>(a, B, s);
 }
 
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
                          int32_t* idx, uint8_t* mask, hipStream_t s) {
-    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr, nullptr, nullptr};
-    return stage2_pk<1, 1, false>(a, B, s);
+    Stage2Args a{nullptr, nullptr, nullptr, nullptr, key, d, F, f_pad, k_ff, W2, idx, mask, nullptr, nullptr, nullptr,
+                 nullptr, nullptr};
+    return stage2_pk<1, 1, 0>(a, B, s);
 }
 
 // ---------------------------------------------------------------------------

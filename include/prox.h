@@ -58,8 +58,11 @@ typedef enum {
 } prox_status;
 
 typedef enum {
-    PROX_PROXY_INT8 = 1,      /* one fp32 scale per output channel, codes in [-127, 127]        */
-    PROX_PROXY_INT4_G128 = 2  /* one fp32 scale per (128 inputs, channel), codes in [-7, 7]     */
+    PROX_PROXY_INT8 = 1,       /* one fp32 scale per output channel, codes in [-127, 127]        */
+    PROX_PROXY_INT4_G128 = 2,  /* one fp32 scale per (128 inputs, channel), codes in [-7, 7]     */
+    PROX_PROXY_EXACT_BF16 = 3  /* exact-mask mode: no proxy; every input kept (k_in = d_model)
+                                  and the channels ranked by the exact |h| computed from the bf16
+                                  weights themselves (the selector the proxies approximate)      */
 } prox_proxy_kind;
 
 /* Limits of this build: 8 <= d_model <= 16384, d_model % 8 == 0 (int4: % 128);
@@ -143,14 +146,17 @@ typedef struct {
 /* ABI version compiled into the library (PROX_ABI_VERSION). */
 int32_t prox_abi_version(void);
 
-/* Bytes a proxy of this shape and kind needs; 0 if the arguments are invalid. */
+/* Bytes a proxy of this shape and kind needs; 0 if the arguments are invalid
+ * (and for PROX_PROXY_EXACT_BF16, which needs no buffer). */
 size_t prox_proxy_bytes(int32_t d_model, int32_t d_ff, int32_t kind);
 
 /* Build the proxy of w->w_gate_t and w->w_up_t ("quantized proxy weights",
  * Prox, Abstract) into the caller's device buffer `buf` (buf_bytes >=
  * prox_proxy_bytes, 256-byte aligned) and fill the host descriptor `out`.
  * One-time, training-free transform of the weights; the codes are bit-exact
- * with the scale/code rule stated at the top of this header. */
+ * with the scale/code rule stated at the top of this header.
+ * PROX_PROXY_EXACT_BF16: nothing is built or enqueued; `buf` may be NULL and
+ * the descriptor only records the shape (bytes = 0). */
 prox_status prox_build_proxy(const prox_weights* w, int32_t kind, void* buf, size_t buf_bytes,
                              prox_proxy* out, void* stream);
 
@@ -175,6 +181,13 @@ prox_status prox_ffn_forward(const void* x, int32_t batch, const prox_weights* w
                              const prox_proxy* p, int32_t k_in, int32_t k_ff, float* y,
                              uint8_t* mask, int32_t* idx, void* workspace, size_t ws_bytes,
                              void* stream);
+
+/* With a PROX_PROXY_EXACT_BF16 descriptor (exact-mask mode) k_in must equal
+ * d_model (PROX_E_INVALID otherwise): Stage 1 computes h_j = silu(x . W_gate[:, j])
+ * (x . W_up[:, j]) for every channel in fp64 and ranks fp32(|h_j|); Stage 2
+ * keeps the top k_ff and streams only their W_down rows, with h read back.
+ * The per-token kernels run for every batch size.  k_ff = d_ff gives the
+ * dense FFN. */
 
 /* prox_ffn_forward plus the intermediate outputs in `taps` (nullable). */
 prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const prox_weights* w,
@@ -205,6 +218,21 @@ size_t prox_noalloc_scratch_bytes(void);
 prox_status prox_ffn_forward_noalloc(const void* x, int32_t batch, const prox_weights* w,
                                      const prox_proxy* p, int32_t k_in, int32_t k_ff, float* y,
                                      uint8_t* mask, int32_t* idx, void* stream);
+
+/* ---- Quality diagnostics (not part of the forward) --------------------------
+ * For each token b < batch, on device data:
+ *   overlap[b] = number of channels j < d_ff with mask_a[b][j] != 0 and
+ *                mask_b[b][j] != 0 (kept channels in common: the mask recall
+ *                of a proxy against the exact-mask mode is overlap / k_ff);
+ *   err[b]     = ||y[b] - y_ref[b]||_2 / ||y_ref[b]||_2 in fp64 (the numerator
+ *                alone when y_ref[b] is 0), e.g. a sparse forward against the
+ *                dense FFN (exact mode with k_ff = d_ff).
+ * mask_a, mask_b: uint8 [batch][d_ff]; y, y_ref: fp32 [batch][d_model];
+ * overlap int32 [batch]; err fp64 [batch]; all device.  Each triple (masks +
+ * overlap, ys + err) is given or null as a whole, at least one of them.    */
+prox_status prox_quality(const uint8_t* mask_a, const uint8_t* mask_b, int32_t batch, int32_t d_ff,
+                         const float* y, const float* y_ref, int32_t d_model, int32_t* overlap,
+                         double* err, void* stream);
 
 /* ---- Measurement helper (not part of the forward) ---------------------------
  * Read-stream probe: reads the first bytes / 16 * 16 bytes of the device

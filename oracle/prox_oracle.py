@@ -310,3 +310,26 @@ def mask_diff(tok: TokenResult, gpu_mask: np.ndarray, band: float = 1e-6):
         if np.isfinite(t) and abs(abs(tok.h_hat[j]) - t) <= band * t:
             exc += 1
     return exc, len(diff) - exc, diff
+
+
+# --------------------------------------------------------------------------
+# Quality of a mask and of an output (plain definitions; the pages give no
+# numbers for them, so the values are diagnostics, not parity targets).
+# --------------------------------------------------------------------------
+
+def mask_overlap(mask_a: np.ndarray, mask_b: np.ndarray) -> int:
+    """Number of channels kept by both masks (index arrays or 0/1 vectors)."""
+    a, b = np.asarray(mask_a), np.asarray(mask_b)
+    if a.dtype == np.uint8 or a.dtype == bool:
+        return int(np.count_nonzero((a != 0) & (b != 0)))
+    return len(set(a.tolist()) & set(b.tolist()))
+
+
+def rel_l2_error(y: np.ndarray, y_ref: np.ndarray) -> float:
+    """||y - y_ref||_2 / ||y_ref||_2 (the numerator alone when y_ref is 0)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    num = float(np.sqrt(np.sum((y - y_ref) ** 2)))
+    den = float(np.sqrt(np.sum(y_ref ** 2)))
+    return num / den if den > 0 else num
+

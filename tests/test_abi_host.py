@@ -131,3 +131,24 @@ def test_noalloc_rejects_oversized_shape_before_any_launch():
                                        FAKE, FAKE, FAKE, None)
     assert st == UNSUPPORTED
     assert b"scratch" in _lib.prox_last_error()
+
+
+def test_exact_kind_host_side():
+    # exact-mask mode needs no proxy buffer; a forward with k_in != d_model is
+    # rejected on the host
+    assert P.proxy_bytes(4096, 11008, "exact") == 0
+    assert P.workspace_bytes(4096, 11008, 1, "exact") > P.workspace_bytes(4096, 11008, 1, "int8") - 1
+    w = _Weights(512, 1000, FAKE, FAKE, FAKE)
+    desc = _Proxy()
+    assert _lib.prox_build_proxy(ctypes.byref(w), 3, None, 0, ctypes.byref(desc), None) == 0
+    assert desc.kind == 3 and desc.bytes == 0 and desc.f_pad == 1024
+    st = _lib.prox_ffn_forward(FAKE, 1, ctypes.byref(w), ctypes.byref(desc), 100, 10, FAKE, FAKE, FAKE,
+                               FAKE, 1 << 30, None)
+    assert st == INVALID and b"k_in" in _lib.prox_last_error()
+
+
+def test_quality_rejects_partial_arguments():
+    assert _lib.prox_quality(FAKE, None, 1, 10, None, None, 8, FAKE, None, None) == INVALID
+    assert _lib.prox_quality(None, None, 1, 10, FAKE, FAKE, 8, None, None, None) == INVALID
+    assert _lib.prox_quality(None, None, 1, 10, None, None, 8, None, None, None) == INVALID
+    assert _lib.prox_quality(None, None, 0, 10, FAKE, FAKE, 8, None, FAKE, None) == INVALID

@@ -604,3 +604,31 @@ def test_mutant_bf16_shift(monkeypatch):
         return b.view(np.float32).astype(np.float64)
     monkeypatch.setattr(O, "bf16_bits_to_f64", bad)
     assert _caught(test_p7_bf16_bits_hand_values)
+
+
+# ---------------------------------------------------------------------------
+# P12. Quality diagnostics: closed forms.
+# ---------------------------------------------------------------------------
+
+def test_p12_mask_overlap_and_error_closed_forms():
+    a = np.array([1, 4, 7, 9])
+    assert O.mask_overlap(a, a) == 4
+    assert O.mask_overlap(a, np.array([0, 2, 3])) == 0
+    assert O.mask_overlap(a, np.array([4, 9, 10])) == 2
+    va, vb = np.zeros(12, np.uint8), np.zeros(12, np.uint8)
+    va[[1, 4, 7]] = 1
+    vb[[4, 7, 8]] = 1
+    assert O.mask_overlap(va, vb) == 2
+    y = np.array([3.0, 4.0])
+    assert O.rel_l2_error(y, y) == 0.0
+    assert O.rel_l2_error(2 * y, y) == 1.0                 # ||y|| / ||y||
+    assert O.rel_l2_error(y + np.array([0.0, 5.0]), y) == 1.0
+    assert O.rel_l2_error(y, np.zeros(2)) == 5.0            # y_ref = 0: the numerator
+
+
+def test_p12_exact_mode_full_k_is_dense():
+    # the exact-mask mode keeping every channel is the dense FFN (P1 for the
+    # exact kind, every input kept)
+    x, wg, wu, wd = _case(128, 64, 2, 31)
+    res = O.oracle_forward(x, wg, wu, wd, "exact", 128, 64)
+    assert O.rel_l2_error(res.y, _torch_dense(x, wg, wu, wd)) <= 1e-13
