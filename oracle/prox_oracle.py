@@ -333,3 +333,62 @@ def rel_l2_error(y: np.ndarray, y_ref: np.ndarray) -> float:
     den = float(np.sqrt(np.sum(y_ref ** 2)))
     return num / den if den > 0 else num
 
+
+# --------------------------------------------------------------------------
+# Quantized Stage-2 weights (Prox, Abstract: the method is compatible with
+# quantization).  Each row of W_gate^T, W_up^T (the weights of one channel)
+# and of W_down (the output direction of one channel) gets one fp32 scale,
+# with the rule of the int8 proxy: s = fl32(max |row| / 127),
+# q = clamp(rne(fl32(w / s)), -127, 127); the row's weights become s * q.
+# Stage 1 is unchanged (its proxy comes from the bf16 weights); Stage 2
+# computes the kept channels with the quantized rows.
+# --------------------------------------------------------------------------
+
+@dataclass
+class QWeights:
+    qg: np.ndarray       # [F][d] int8 codes of W_gate^T rows
+    sg: np.ndarray       # [F] fp32
+    qu: np.ndarray
+    su: np.ndarray
+    qd: np.ndarray       # [F][d] int8 codes of W_down rows
+    sd: np.ndarray
+    wg_t: np.ndarray     # [F][d] float64 s * q (dequantized rows)
+    wu_t: np.ndarray
+    wd: np.ndarray
+
+
+def quantize_rows_int8(w_rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """int8 codes and fp32 scales, one scale per row of w_rows [F][d]."""
+    q, s = quantize_int8_pc(np.asarray(w_rows).T)      # the per-column rule on the transpose
+    return np.ascontiguousarray(q.T), s
+
+
+def build_qweights(wg_t: np.ndarray, wu_t: np.ndarray, wd: np.ndarray) -> QWeights:
+    out = {}
+    for name, w in (("g", wg_t), ("u", wu_t), ("d", wd)):
+        q, s = quantize_rows_int8(w)
+        out["q" + name], out["s" + name] = q, s
+        out[name] = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    return QWeights(out["qg"], out["sg"], out["qu"], out["su"], out["qd"], out["sd"], out["g"], out["u"], out["d"])
+
+
+def oracle_forward_q8(x: np.ndarray, wg_t: np.ndarray, wu_t: np.ndarray, wd: np.ndarray, kind: str, k_in: int,
+                      k_ff: int, proxies: Optional[Tuple[Proxy, Proxy]] = None,
+                      qw: Optional[QWeights] = None) -> ForwardResult:
+    """The forward with quantized Stage-2 weights: Stage 1 from the proxy of
+    the bf16 weights, Stage 2 (stage2_batch) on the dequantized rows."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    wg_t, wu_t, wd = (np.asarray(a, dtype=np.float64) for a in (wg_t, wu_t, wd))
+    if not (0 <= k_in <= x.shape[1] and 0 <= k_ff <= wg_t.shape[0]):
+        raise ValueError("k out of range")
+    if proxies is None:
+        proxies = (build_proxy(wg_t.T, kind), build_proxy(wu_t.T, kind))
+    if qw is None:
+        qw = build_qweights(wg_t, wu_t, wd)
+    s1 = stage1_batch(x, proxies[0], proxies[1], k_in, k_ff)
+    hs, y = stage2_batch(x, qw.wg_t, qw.wu_t, qw.wd, [r[5] for r in s1])
+    res = ForwardResult()
+    for b, (s_in, g_hat, u_hat, h_hat, key, mask, t) in enumerate(s1):
+        res.tokens.append(TokenResult(s_in, g_hat, u_hat, h_hat, key, mask, t, hs[b], y[b]))
+    return res
+

@@ -632,3 +632,75 @@ def test_p12_exact_mode_full_k_is_dense():
     x, wg, wu, wd = _case(128, 64, 2, 31)
     res = O.oracle_forward(x, wg, wu, wd, "exact", 128, 64)
     assert O.rel_l2_error(res.y, _torch_dense(x, wg, wu, wd)) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# P13. Quantized Stage-2 weights.
+# ---------------------------------------------------------------------------
+
+def test_p13_row_quantizer_worked_values():
+    # row max 127 * 2^-7: s = 2^-7, codes = w * 2^7, ties to even; one scale
+    # per ROW (a second row with its own scale)
+    r0 = np.array([127, -64, 3, 2.5, -2.5, 3.5, 0, 1], dtype=np.float64) / 128.0
+    r1 = np.array([0, 0, 7, -7, 1.5, 0.5, 0, 0], dtype=np.float64) / 16.0      # max 7/16: s = 7/16/127
+    q, s = O.quantize_rows_int8(np.stack([r0, r1]))
+    assert s[0] == np.float32(2.0 ** -7)
+    assert q[0].tolist() == [127, -64, 3, 2, -2, 4, 0, 1]
+    assert s[1] == np.float32(np.float32(7 / 16) / np.float32(127))
+    assert q[1, 2] == 127 and q[1, 3] == -127
+    assert q.shape == (2, 8) and s.shape == (2,)
+
+
+def _exact_codes_case(d, F, B, seed):
+    # weights that are exactly s * q with s = 2^-7 and every row reaching 127:
+    # the row quantizer reproduces them, so the quantized forward is the
+    # bf16 forward
+    r = np.random.default_rng(seed)
+    mats = []
+    for _ in range(3):
+        q = r.integers(-127, 128, size=(F, d)).astype(np.float64)
+        q[:, 0] = 127
+        mats.append(q / 128.0)
+    x = _f64(bf16_round(r.laplace(size=(B, d)).astype(np.float32)))
+    return x, mats[0], mats[1], mats[2]
+
+
+def check_q8_reduces_to_bf16():
+    x, wg, wu, wd = _exact_codes_case(96, 64, 2, 4)
+    qw = O.build_qweights(wg, wu, wd)
+    for a, b in ((qw.wg_t, wg), (qw.wu_t, wu), (qw.wd, wd)):
+        assert np.array_equal(a, b)
+    a = O.oracle_forward(x, wg, wu, wd, "int8", 60, 20)
+    b = O.oracle_forward_q8(x, wg, wu, wd, "int8", 60, 20, qw=qw)
+    assert [t.mask.tolist() for t in a.tokens] == [t.mask.tolist() for t in b.tokens]
+    assert np.max(np.abs(a.y - b.y)) <= 1e-13 * np.max(np.abs(a.y))
+
+
+def test_p13_exact_codes_reduce_to_bf16():
+    check_q8_reduces_to_bf16()
+
+
+def test_p13_q8_stage2_is_dequantized_rows():
+    # y by scalar loops over the kept channels with s * q rows (fsum)
+    x, wg, wu, wd = _case(16, 12, 1, 8)
+    res = O.oracle_forward_q8(x, wg, wu, wd, "int8", 9, 5)
+    tok = res.tokens[0]
+    qw = O.build_qweights(wg, wu, wd)
+    for c in range(16):
+        terms = []
+        for j in tok.mask:
+            g = math.fsum(float(x[0, i]) * float(qw.sg[j]) * float(qw.qg[j, i]) for i in range(16))
+            u = math.fsum(float(x[0, i]) * float(qw.su[j]) * float(qw.qu[j, i]) for i in range(16))
+            terms.append(_silu_scalar(g) * u * float(qw.sd[j]) * float(qw.qd[j, c]))
+        assert abs(math.fsum(terms) - tok.y[c]) <= 1e-12 * max(np.max(np.abs(tok.y)), 1e-300)
+    # the mask is the one Stage 1 ranks from the bf16 weights' proxy
+    assert tok.mask.tolist() == O.oracle_forward(x, wg, wu, wd, "int8", 9, 5).tokens[0].mask.tolist()
+
+
+def test_mutant_q8_per_column_scales(monkeypatch):
+    # one scale per column (the proxy's orientation) instead of per row
+    def bad(w_rows):
+        q, s = O.quantize_int8_pc(np.asarray(w_rows))
+        return q, s
+    monkeypatch.setattr(O, "quantize_rows_int8", bad)
+    assert _caught(test_p13_row_quantizer_worked_values)
