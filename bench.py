@@ -43,15 +43,19 @@ LLC_BYTES = 256 << 20
 BATCH_MIN = 4   # the library's switch to the matrix-core path (tokens per call)
 
 
-def algorithmic_bytes(d, F, kind, k_in_rows, k_ch):
-    """Weight bytes one forward must read at minimum: proxy codes of the kept
-    rows + proxy scales (Stage 1) and 3 bf16 rows per kept channel (Stage 2).
-    For several tokens the kept rows / channels are the union over the batch
-    (measured from the call's own outputs)."""
+def algorithmic_bytes(d, F, kind, k_in_rows, k_ch, mode="proxy"):
+    """Weight bytes one forward must read at minimum.  Stage 1: the proxy codes
+    of the kept rows + the proxy scales (exact mode: every gate and up row,
+    bf16).  Stage 2: 3 rows per kept channel, bf16 (q8: int8 rows + 3 fp32
+    scales; exact mode: the W_down row only, h being known).  For several
+    tokens the kept rows / channels are the union over the batch (measured
+    from the call's own outputs)."""
+    if mode == "exact":
+        return 2 * F * d * 2, k_ch * d * 2
     bits = 8 if kind == "int8" else 4
     groups = 1 if kind == "int8" else d // 128
     proxy = 2 * k_in_rows * F * bits // 8 + 2 * groups * F * 4
-    stage2 = 3 * k_ch * d * 2
+    stage2 = 3 * k_ch * d + 3 * k_ch * 4 if mode == "q8" else 3 * k_ch * d * 2
     return proxy, stage2
 
 
@@ -61,6 +65,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2_s70")
+    ap.add_argument("--mode", default="proxy", choices=["proxy", "exact", "q8"],
+                    help="proxy: the workload's proxy and bf16 Stage 2; exact: exact-mask mode (every input "
+                         "kept); q8: int8 Stage-2 rows")
     ap.add_argument("--layers", type=int, default=0, help="stacked workloads: first N layers only (0 = all)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -88,7 +95,8 @@ def main(argv=None):
     wl = workloads()[args.workload]
     n_layers = wl.n_layers if not args.layers else min(args.layers, wl.n_layers)
     stack = wl.n_layers > 1
-    B, kind = wl.batch, wl.proxy
+    B, kind = wl.batch, (wl.proxy if args.mode != "exact" else "exact")
+    k_in_of = (lambda l: wl.layers[l].d) if args.mode == "exact" else wl.k_in
 
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -102,13 +110,18 @@ def main(argv=None):
         if layer == 0:
             w0 = w
         base = P.Weights(up(w["wg_t"]), up(w["wu_t"]), up(w["wd"]))
-        copies_l = [(base, P.build_proxy(base, kind))]
+
+        def s2rows(wt):
+            return P.build_qweights(wt) if args.mode == "q8" else wt
+        copies_l = [(s2rows(base), P.build_proxy(base, kind))]
         if not stack:
             layer_bytes = 3 * F * d * 2 + copies_l[0][1].desc.bytes
             copies = args.copies or max(4, int(np.ceil(4 * LLC_BYTES / layer_bytes)))
             for _ in range(min(copies, 64) - 1):
                 wc = P.Weights(base.w_gate_t.clone(), base.w_up_t.clone(), base.w_down.clone())
-                copies_l.append((wc, P.build_proxy(wc, kind)))
+                copies_l.append((s2rows(wc), P.build_proxy(wc, kind)))
+        if args.mode == "q8":
+            del base
         sets.append(copies_l)
         del w
     n_copies = len(sets[0])
@@ -131,7 +144,7 @@ def main(argv=None):
         d, F = wl.layers[layer].d, wl.layers[layer].F
         wt, px = sets[layer][i % n_copies]
         y, mask, idx = bufs[(d, F)]
-        P.ffn_forward(xs[layer][i % n_x], wt, px, wl.k_in(layer), wl.k_ff(layer), y=y, mask=mask, idx=idx,
+        P.ffn_forward(xs[layer][i % n_x], wt, px, k_in_of(layer), wl.k_ff(layer), y=y, mask=mask, idx=idx,
                       workspace=ws[:P.workspace_bytes(d, F, B, kind)], events=events)
 
     def step(i, events=None):
@@ -179,7 +192,7 @@ def main(argv=None):
     proxy_b = stage2_b = io_b = 0
     for layer in range(n_layers):
         d, F = wl.layers[layer].d, wl.layers[layer].F
-        k_in, k_ff = wl.k_in(layer), wl.k_ff(layer)
+        k_in, k_ff = k_in_of(layer), wl.k_ff(layer)
         forward(layer, 0)
         torch.cuda.synchronize()
         m = bufs[(d, F)][1].cpu().numpy().astype(bool)
@@ -190,7 +203,7 @@ def main(argv=None):
             xb = xs[layer][0].float().abs().cpu().numpy()
             order = np.lexsort((np.tile(np.arange(d), (B, 1)), -xb), axis=1)[:, :k_in]
             rows_union = int(len(np.unique(order)))
-        pb, sb = algorithmic_bytes(d, F, kind, rows_union, ch_union)
+        pb, sb = algorithmic_bytes(d, F, kind, rows_union, ch_union, args.mode)
         proxy_b += pb
         stage2_b += sb
         io_b += B * (2 * d + 4 * d + F + 4 * k_ff)       # x, y, mask, idx
@@ -206,13 +219,15 @@ def main(argv=None):
     dom_name = P.PHASES[dom]
     dom_bytes = {0: proxy_b, 1: stage2_b}.get(dom, total_b)
     dom_gbs = dom_bytes / (phase_ms[dom] * 1e-3) / 1e9
-    if B < BATCH_MIN:
-        dom_kernel = {0: "k_stage1", 1: "k_stage2"}.get(dom, "k_reduce_y")
+    if args.mode == "exact":
+        dom_kernel = {0: "k_exact_h", 1: "k_stage2"}.get(dom, "k_reduce_y")
+    elif B < BATCH_MIN or args.mode == "q8" and dom == 1:
+        dom_kernel = {0: "k_stage1" if B < BATCH_MIN else "k_xsel + k_proxy_batch", 1: "k_stage2"}.get(dom, "k_reduce_y")
     else:
         dom_kernel = {0: "k_xsel + k_proxy_batch",
                       1: "k_stage2 (selection) + k_gateup_batch + k_down_batch"}.get(dom, "k_reduce_y")
     src_hash = kernel_sources_hash()
-    prof = committed_profile(wl.name, dom_kernel, src_hash, n_layers)
+    prof = committed_profile(wl.name, dom_kernel, src_hash, n_layers) if args.mode == "proxy" else {}
     probe = None if args.no_read_probe else read_probe_gbs(P, torch, dev)
 
     out = {
@@ -231,15 +246,20 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "dtype_detail": "Stage 2: bf16 weights, fp32 accumulation; Stage 1: int8/int4 codes x bf16 x, "
-                        "fp32 exact chunk sums into fp64 totals",
+        "dtype_detail": {"proxy": "Stage 2: bf16 weights, fp32 accumulation; Stage 1: int8/int4 codes x bf16 x, "
+                                  "fp32 exact chunk sums into fp64 totals",
+                         "exact": "Stage 1: bf16 gate/up rows x bf16 x, fp64 accumulation; Stage 2: bf16 W_down rows, "
+                                  "fp32 accumulation",
+                         "q8": "Stage 2: int8 rows x fp32 row scales, fp32 accumulation; Stage 1 as proxy"}[args.mode],
         "data": "synthetic (seeded N(0,0.02) bf16 weights, Laplace x with outliers or RMS-normalised; "
                 "random-init, no checkpoint)",
         "config": {"workload": f"{wl.name}: d_model={'/'.join(str(s[0]) for s in shapes)} "
                                f"d_ff={'/'.join(str(s[1]) for s in shapes)} layers={n_layers} batch={B} "
-                               f"proxy={kind} keep={wl.keep_pct}% sparsity={wl.sparsity_pct}%",
+                               f"proxy={kind} keep={100 if args.mode == 'exact' else wl.keep_pct}% "
+                               f"sparsity={wl.sparsity_pct}% stage2={'int8 rows' if args.mode == 'q8' else 'bf16'}",
+                   "mode": args.mode,
                    "layers": n_layers, "batch": B, "proxy": kind,
-                   "k_in": [wl.k_in(l) for l in range(min(n_layers, 2))],
+                   "k_in": [k_in_of(l) for l in range(min(n_layers, 2))],
                    "k_ff": [wl.k_ff(l) for l in range(min(n_layers, 2))],
                    "weight_copies_rotated": n_copies, "algorithmic_bytes_per_step": int(total_b)},
         "phase_us": {P.PHASES[p]: round(float(phase_ms[p] * 1e3), 2) for p in range(P.N_PHASES)},
@@ -260,7 +280,7 @@ def main(argv=None):
         "setup_s": round(setup_s, 1),
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.mode == "proxy":
         out["cpu_baseline"] = cpu_baseline(wl, w0, xs[0], total_b / n_layers / B, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0

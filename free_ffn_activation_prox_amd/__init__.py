@@ -48,6 +48,11 @@ class _Proxy(ctypes.Structure):
                 ("bytes", ctypes.c_size_t), ("buf", ctypes.c_void_p)]
 
 
+class _QWeights(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("scale_offset", ctypes.c_size_t),
+                ("bytes", ctypes.c_size_t), ("buf", ctypes.c_void_p)]
+
+
 class _Taps(ctypes.Structure):
     _fields_ = [("in_idx", ctypes.c_void_p), ("key", ctypes.c_void_p), ("h_hat", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
@@ -78,6 +83,10 @@ def _load() -> ctypes.CDLL:
                                            P, P, P, P]),
         "prox_read_probe": (I32, [P, SZ, P, I32, P]),
         "prox_quality": (I32, [P, P, I32, I32, P, P, I32, P, P, P]),
+        "prox_qweights_bytes": (SZ, [I32, I32]),
+        "prox_build_qweights": (I32, [ctypes.POINTER(_Weights), P, SZ, ctypes.POINTER(_QWeights), P]),
+        "prox_ffn_forward_q8": (I32, [P, I32, ctypes.POINTER(_QWeights), ctypes.POINTER(_Proxy), I32, I32, P, P, P,
+                                      P, SZ, ctypes.POINTER(_Taps), P]),
         "prox_status_str": (ctypes.c_char_p, [I32]),
         "prox_last_error": (ctypes.c_char_p, []),
     }
@@ -188,6 +197,50 @@ def build_proxy(weights: Weights, kind: str, stream=None) -> Proxy:
     return Proxy(kind, buf, desc)
 
 
+@dataclass
+class QWeights:
+    """Quantized Stage-2 weights: int8 rows of W_gate^T, W_up^T, W_down and
+    their fp32 scales in one device buffer (prox_build_qweights)."""
+
+    buf: "object"
+    desc: _QWeights
+
+    @property
+    def d_model(self) -> int:
+        return self.desc.d_model
+
+    @property
+    def d_ff(self) -> int:
+        return self.desc.d_ff
+
+    def codes_and_scales(self):
+        """Device views: codes [3][F][d] int8, scales [3][F] fp32."""
+        import torch
+        d, F = self.desc.d_model, self.desc.d_ff
+        codes = self.buf[: 3 * F * d].view(torch.int8).view(3, F, d)
+        so = self.desc.scale_offset
+        scales = self.buf[so: so + 12 * F].view(torch.float32).view(3, F)
+        return codes, scales
+
+
+def qweights_bytes(d_model: int, d_ff: int) -> int:
+    return _lib.prox_qweights_bytes(d_model, d_ff)
+
+
+def build_qweights(weights: Weights, stream=None) -> QWeights:
+    import torch
+    n = qweights_bytes(weights.d_model, weights.d_ff)
+    if n == 0:
+        raise ValueError("invalid shape for quantized weights")
+    raw = torch.empty(n + 256, dtype=torch.uint8, device=weights.w_gate_t.device)
+    off = (-raw.data_ptr()) % 256
+    buf = raw[off: off + n]
+    desc = _QWeights()
+    _check(_lib.prox_build_qweights(ctypes.byref(weights._c), buf.data_ptr(), n, ctypes.byref(desc),
+                                    _stream_ptr(stream)), "prox_build_qweights")
+    return QWeights(buf, desc)
+
+
 def alloc_workspace(d_model: int, d_ff: int, batch: int, kind: str, device="cuda"):
     import torch
     n = workspace_bytes(d_model, d_ff, batch, kind)
@@ -199,7 +252,7 @@ def alloc_workspace(d_model: int, d_ff: int, batch: int, kind: str, device="cuda
     return raw[off: off + n]
 
 
-def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=None, mask=None,
+def ffn_forward(x, weights, proxy: Proxy, k_in: int, k_ff: int, *, y=None, mask=None,
                 idx=None, workspace=None, taps: bool = False, events=None, stream=None):
     """Sparse SwiGLU forward for x [B][d] bf16.  Returns (y fp32 [B][d], mask u8 [B][F],
     idx int32 [B][k_ff]) and, with ``taps``, a dict of in_idx / key / h_hat.
@@ -212,6 +265,7 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     B, d = x.shape
     F = weights.d_ff
     dev = x.device
+    q8 = isinstance(weights, QWeights)
     if y is None:
         y = torch.empty(B, d, dtype=torch.float32, device=dev)
     if mask is None:
@@ -224,11 +278,7 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*[getattr(e, "cuda_event", e) for e in events])
         ct = _Taps(None, None, None, arr, len(events), 0, None, None)
-        _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
-                                          ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),
-                                          mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
-                                          workspace.numel(), ctypes.byref(ct), sp),
-               "prox_ffn_forward_taps")
+        _call_forward(q8, x, B, weights, proxy, k_in, k_ff, y, mask, idx, workspace, ct, sp)
         return y, mask, idx[:, :k_ff]
     if taps:
         t = {"in_idx": torch.empty(B, max(k_in, 1), dtype=torch.int32, device=dev),
@@ -237,19 +287,32 @@ def ffn_forward(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int, *, y=No
              "stream_idx": torch.full((B, max(k_ff, 1)), -1, dtype=torch.int32, device=dev)}
         ct = _Taps(t["in_idx"].data_ptr(), t["key"].data_ptr(), t["h_hat"].data_ptr(), None, 0, 0,
                    t["stream_idx"].data_ptr(), None)
-        _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c),
-                                          ctypes.byref(proxy.desc), k_in, k_ff, y.data_ptr(),
-                                          mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
-                                          workspace.numel(), ctypes.byref(ct), sp),
-               "prox_ffn_forward_taps")
+        _call_forward(q8, x, B, weights, proxy, k_in, k_ff, y, mask, idx, workspace, ct, sp)
         t["in_idx"] = t["in_idx"][:, :k_in]
         t["stream_idx"] = t["stream_idx"][:, :k_ff]
         return y, mask, idx[:, :k_ff], t
-    _check(_lib.prox_ffn_forward(x.data_ptr(), B, ctypes.byref(weights._c), ctypes.byref(proxy.desc),
-                                 k_in, k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(),
-                                 workspace.data_ptr(), workspace.numel(), sp),
-           "prox_ffn_forward")
+    if q8:
+        _call_forward(True, x, B, weights, proxy, k_in, k_ff, y, mask, idx, workspace, None, sp)
+    else:
+        _check(_lib.prox_ffn_forward(x.data_ptr(), B, ctypes.byref(weights._c), ctypes.byref(proxy.desc),
+                                     k_in, k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), sp),
+               "prox_ffn_forward")
     return y, mask, idx[:, :k_ff]
+
+
+def _call_forward(q8, x, B, weights, proxy, k_in, k_ff, y, mask, idx, workspace, ct, sp):
+    tp = ctypes.byref(ct) if ct is not None else None
+    if q8:
+        _check(_lib.prox_ffn_forward_q8(x.data_ptr(), B, ctypes.byref(weights.desc), ctypes.byref(proxy.desc), k_in,
+                                        k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel(), tp, sp),
+               "prox_ffn_forward_q8")
+    else:
+        _check(_lib.prox_ffn_forward_taps(x.data_ptr(), B, ctypes.byref(weights._c), ctypes.byref(proxy.desc),
+                                          k_in, k_ff, y.data_ptr(), mask.data_ptr(), idx.data_ptr(),
+                                          workspace.data_ptr(), workspace.numel(), tp, sp),
+               "prox_ffn_forward_taps")
 
 
 def read_probe(buf, sink, blocks: int, stream=None) -> None:
@@ -319,5 +382,5 @@ def ffn_forward_noalloc(x, weights: Weights, proxy: Proxy, k_in: int, k_ff: int,
     return y, mask, idx[:, :k_ff]
 
 
-__all__ = ["quality", "timeline_forward", "read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
+__all__ = ["QWeights", "build_qweights", "qweights_bytes", "quality", "timeline_forward", "read_probe", "noalloc_scratch_bytes", "ffn_forward_noalloc", "Weights", "Proxy", "ProxError", "abi_version", "library_sha256", "proxy_bytes", "workspace_bytes",
            "build_proxy", "alloc_workspace", "ffn_forward", "LIB_PATH", "KINDS", "N_PHASES", "PHASES"]

@@ -156,17 +156,22 @@ extern "C" prox_status prox_build_proxy(const prox_weights* w, int32_t kind, voi
     return PROX_OK;
 }
 
-extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const prox_weights* w,
-                                             const prox_proxy* p, int32_t k_in, int32_t k_ff,
-                                             float* y, uint8_t* mask, int32_t* idx,
-                                             void* workspace, size_t ws_bytes,
-                                             const prox_taps* taps, void* stream) {
-    g_err.clear();
-    if (!x || !w || !p || !y || !workspace)
-        return fail(PROX_E_INVALID, "null x, weights, proxy, y or workspace");
-    if (!w->w_gate_t || !w->w_up_t || !w->w_down) return fail(PROX_E_INVALID, "null weight buffer");
+namespace {
+
+// Stage-2 rows of one forward: bf16 [F][d] each (qscale null), or int8 [F][d]
+// each with their row scales qscale [3][F] (quantized Stage-2 weights).
+struct S2Rows {
+    const void* g;
+    const void* u;
+    const void* dn;
+    const float* qscale;
+};
+
+prox_status forward_impl(const void* x, int32_t batch, int d, int F, const S2Rows& rows, const prox_proxy* p,
+                         int32_t k_in, int32_t k_ff, float* y, uint8_t* mask, int32_t* idx, void* workspace,
+                         size_t ws_bytes, const prox_taps* taps, void* stream) {
+    if (!x || !p || !y || !workspace) return fail(PROX_E_INVALID, "null x, proxy, y or workspace");
     if (!p->buf && p->kind != PROX_PROXY_EXACT_BF16) return fail(PROX_E_INVALID, "null proxy buffer");
-    const int d = w->d_model, F = w->d_ff;
     if (const char* e = shape_error(d, F, p->kind)) return fail(PROX_E_INVALID, "%s", e);
     if (const char* e = limit_error(d, F)) return fail(PROX_E_UNSUPPORTED, "%s", e);
     if (batch < 1) return fail(PROX_E_INVALID, "batch must be >= 1");
@@ -175,14 +180,15 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     if (k_ff < 0 || k_ff > F) return fail(PROX_E_INVALID, "k_ff out of [0, d_ff]");
     if (p->kind == PROX_PROXY_EXACT_BF16 && k_in != d)
         return fail(PROX_E_INVALID, "exact mode keeps every input: k_in must equal d_model");
+    if (p->kind == PROX_PROXY_EXACT_BF16 && rows.qscale)
+        return fail(PROX_E_UNSUPPORTED, "exact mode computes h from the bf16 weights: no quantized Stage 2");
     if (p->d_model != d || p->d_ff != F) return fail(PROX_E_MISMATCH, "proxy shape differs from weights");
     const ProxyGeom g = proxy_geom(d, F, p->kind);
     if (p->f_pad != g.f_pad || p->groups != g.groups || p->tile_ch != g.tile_ch || p->row_stride != g.row_stride ||
         p->scale_offset != g.scale_offset || p->bytes != g.bytes)
         return fail(PROX_E_MISMATCH, "proxy descriptor is not the one prox_build_proxy writes");
-    if (!aligned(x, 16) || !aligned(w->w_gate_t, 16) || !aligned(w->w_up_t, 16) ||
-        !aligned(w->w_down, 16) || !aligned(y, 16) || (p->kind != PROX_PROXY_EXACT_BF16 && !aligned(p->buf, 256)))
-        return fail(PROX_E_INVALID, "misaligned x, weights, y or proxy");
+    if (!aligned(x, 16) || !aligned(y, 16) || (p->kind != PROX_PROXY_EXACT_BF16 && !aligned(p->buf, 256)))
+        return fail(PROX_E_INVALID, "misaligned x, y or proxy");
     if (!aligned(workspace, 256)) return fail(PROX_E_INVALID, "workspace must be 256-byte aligned");
     const WsLayout L = ws_layout(d, F, batch, p->kind);
     if (ws_bytes < L.total) return fail(PROX_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
@@ -208,9 +214,9 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     hipError_t e = mark(0);
     if (e != hipSuccess) return hip_fail(e, "event record");
     unsigned long long* tcnt = reinterpret_cast<unsigned long long*>(ws + L.tcnt);
-    const uint16_t* wg = static_cast<const uint16_t*>(w->w_gate_t);
-    const uint16_t* wu = static_cast<const uint16_t*>(w->w_up_t);
-    const uint16_t* wd = static_cast<const uint16_t*>(w->w_down);
+    const uint16_t* wg = static_cast<const uint16_t*>(rows.g);
+    const uint16_t* wu = static_cast<const uint16_t*>(rows.u);
+    const uint16_t* wd = static_cast<const uint16_t*>(rows.dn);
 
     if (p->kind == PROX_PROXY_EXACT_BF16) {
         // exact mode: h of every channel (fp64), then the selection and the
@@ -229,6 +235,37 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
         if (e != hipSuccess) return hip_fail(e, "exact stage 2");
         if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
         e = launch_reduce_y(ypart, batch, d, W2x, y, s);
+        if (e != hipSuccess) return hip_fail(e, "reduce y");
+        if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
+        return PROX_OK;
+    }
+
+    if (rows.qscale) {
+        // quantized Stage-2 weights: Stage 1 as for the bf16 rows (the
+        // matrix-core proxy GEMM from kBatchMin tokens), Stage 2 with the
+        // per-token kernel streaming int8 rows for every batch
+        if (batch >= kBatchMin) {
+            uint16_t* xm = reinterpret_cast<uint16_t*>(ws + L.xm);
+            e = launch_xsel(xb, batch, d, k_in, xm, taps ? taps->in_idx : nullptr, s);
+            if (e != hipSuccess) return hip_fail(e, "input selection");
+            e = launch_proxy_batch(xm, batch, d, pv, reinterpret_cast<float*>(ws + L.bpart), tcnt, next_call_tag(),
+                                   key, taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr, s);
+            if (e != hipSuccess) return hip_fail(e, "proxy GEMM");
+        } else {
+            const S1Geom g1 = s1_geom(k_in, F, p->kind, batch, n_cu);
+            e = launch_stage1(xb, batch, d, k_in, pv, key, reinterpret_cast<double*>(ws + L.part), tcnt,
+                              next_call_tag(), g1, taps ? taps->h_hat : nullptr, taps ? taps->key : nullptr,
+                              taps ? taps->in_idx : nullptr, taps ? (unsigned long long*)taps->timeline : nullptr, s);
+            if (e != hipSuccess) return hip_fail(e, "stage 1");
+        }
+        if ((e = mark(1 + PROX_PHASE_STAGE1)) != hipSuccess) return hip_fail(e, "event record");
+        const int W2q = stage2_blocks(batch, k_ff, d <= 4096 ? n_cu : n_cu * 3 / 4);
+        e = launch_stage2(xb, rows.g, rows.u, rows.dn, key, batch, d, F, g.f_pad, k_ff, W2q, idx, mask, ypart,
+                          taps ? taps->stream_idx : nullptr, taps ? (unsigned long long*)taps->timeline : nullptr, 3,
+                          nullptr, rows.qscale, s);
+        if (e != hipSuccess) return hip_fail(e, "stage 2 (int8 rows)");
+        if ((e = mark(1 + PROX_PHASE_STAGE2)) != hipSuccess) return hip_fail(e, "event record");
+        e = launch_reduce_y(ypart, batch, d, W2q, y, s);
         if (e != hipSuccess) return hip_fail(e, "reduce y");
         if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
         return PROX_OK;
@@ -274,6 +311,80 @@ extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const
     if (e != hipSuccess) return hip_fail(e, "reduce y");
     if ((e = mark(1 + PROX_PHASE_REDUCE_Y)) != hipSuccess) return hip_fail(e, "event record");
     return PROX_OK;
+}
+
+}  // namespace
+
+extern "C" prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const prox_weights* w,
+                                             const prox_proxy* p, int32_t k_in, int32_t k_ff,
+                                             float* y, uint8_t* mask, int32_t* idx,
+                                             void* workspace, size_t ws_bytes,
+                                             const prox_taps* taps, void* stream) {
+    g_err.clear();
+    if (!w) return fail(PROX_E_INVALID, "null weights");
+    if (!w->w_gate_t || !w->w_up_t || !w->w_down) return fail(PROX_E_INVALID, "null weight buffer");
+    if (!aligned(w->w_gate_t, 16) || !aligned(w->w_up_t, 16) || !aligned(w->w_down, 16))
+        return fail(PROX_E_INVALID, "misaligned weights");
+    const S2Rows rows{w->w_gate_t, w->w_up_t, w->w_down, nullptr};
+    return forward_impl(x, batch, w->d_model, w->d_ff, rows, p, k_in, k_ff, y, mask, idx, workspace, ws_bytes,
+                        taps, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Quantized Stage-2 weights.
+// ---------------------------------------------------------------------------
+namespace {
+size_t qweights_scale_offset(int d, int F) { return align_up((size_t)3 * F * d, 256); }
+}  // namespace
+
+extern "C" size_t prox_qweights_bytes(int32_t d, int32_t F) {
+    if (shape_error(d, F, PROX_PROXY_INT8) || limit_error(d, F)) return 0;
+    return qweights_scale_offset(d, F) + (size_t)3 * F * sizeof(float);
+}
+
+extern "C" prox_status prox_build_qweights(const prox_weights* w, void* buf, size_t buf_bytes, prox_qweights* out,
+                                           void* stream) {
+    g_err.clear();
+    if (!w || !buf || !out) return fail(PROX_E_INVALID, "null weights, buffer or output descriptor");
+    if (!w->w_gate_t || !w->w_up_t || !w->w_down) return fail(PROX_E_INVALID, "null weight buffer");
+    const int d = w->d_model, F = w->d_ff;
+    if (const char* e = shape_error(d, F, PROX_PROXY_INT8)) return fail(PROX_E_INVALID, "%s", e);
+    if (const char* e = limit_error(d, F)) return fail(PROX_E_UNSUPPORTED, "%s", e);
+    if (!aligned(buf, 256)) return fail(PROX_E_INVALID, "buffer must be 256-byte aligned");
+    if (!aligned(w->w_gate_t, 16) || !aligned(w->w_up_t, 16) || !aligned(w->w_down, 16))
+        return fail(PROX_E_INVALID, "misaligned weights");
+    const size_t need = prox_qweights_bytes(d, F);
+    if (buf_bytes < need) return fail(PROX_E_INVALID, "buffer too small: %zu < %zu", buf_bytes, need);
+    prox_qweights q{};
+    q.d_model = d;
+    q.d_ff = F;
+    q.scale_offset = qweights_scale_offset(d, F);
+    q.bytes = need;
+    q.buf = buf;
+    uint8_t* b = static_cast<uint8_t*>(buf);
+    hipError_t e = launch_build_qweights(static_cast<const uint16_t*>(w->w_gate_t),
+                                         static_cast<const uint16_t*>(w->w_up_t),
+                                         static_cast<const uint16_t*>(w->w_down), d, F, reinterpret_cast<int8_t*>(b),
+                                         reinterpret_cast<float*>(b + q.scale_offset), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quantized weights build launch");
+    *out = q;
+    return PROX_OK;
+}
+
+extern "C" prox_status prox_ffn_forward_q8(const void* x, int32_t batch, const prox_qweights* q, const prox_proxy* p,
+                                           int32_t k_in, int32_t k_ff, float* y, uint8_t* mask, int32_t* idx,
+                                           void* workspace, size_t ws_bytes, const prox_taps* taps, void* stream) {
+    g_err.clear();
+    if (!q || !q->buf) return fail(PROX_E_INVALID, "null quantized weights");
+    const int d = q->d_model, F = q->d_ff;
+    if (const char* e = shape_error(d, F, PROX_PROXY_INT8)) return fail(PROX_E_INVALID, "%s", e);
+    if (q->scale_offset != qweights_scale_offset(d, F) || q->bytes != prox_qweights_bytes(d, F) ||
+        !aligned(q->buf, 256))
+        return fail(PROX_E_MISMATCH, "quantized-weights descriptor is not the one prox_build_qweights writes");
+    const uint8_t* b = static_cast<const uint8_t*>(q->buf);
+    const size_t m = (size_t)F * d;
+    const S2Rows rows{b, b + m, b + 2 * m, reinterpret_cast<const float*>(b + q->scale_offset)};
+    return forward_impl(x, batch, d, F, rows, p, k_in, k_ff, y, mask, idx, workspace, ws_bytes, taps, stream);
 }
 
 extern "C" prox_status prox_ffn_forward(const void* x, int32_t batch, const prox_weights* w,

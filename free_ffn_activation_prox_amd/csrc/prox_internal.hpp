@@ -143,6 +143,10 @@ hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, h
 hipError_t launch_select(const float* key, int B, int d, int F, int f_pad, int k_ff, int W2,
                          int32_t* idx, uint8_t* mask, hipStream_t s);
 
+// Quantized Stage-2 weights: codes [3][F][d] int8, scales [3][F] fp32.
+hipError_t launch_build_qweights(const uint16_t* wg_t, const uint16_t* wu_t, const uint16_t* wd, int d, int F,
+                                 int8_t* codes, float* scales, hipStream_t s);
+
 // ---- exact mode and diagnostics (prox_exact.hip)
 hipError_t launch_exact_h(const uint16_t* x, int B, int d, const uint16_t* wg_t, const uint16_t* wu_t, int F,
                           int f_pad, int nb, float* key, double* hbuf, double* h_tap, float* key_tap,

@@ -127,6 +127,61 @@ hipError_t launch_build_proxy(const uint16_t* wg_t, const uint16_t* wu_t, int d,
 }
 
 // ---------------------------------------------------------------------------
+// Quantized Stage-2 weights: int8 codes of every row of W_gate^T, W_up^T and
+// W_down, one fp32 scale per row (the proxy's rule: s = fp32(max|row| / 127),
+// code = clamp(round-half-even(fp32(w / s)), -127, 127)).
+// Scales: grid (ceil(F / 4), 3), block 256, one wave per row.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_qrow_scales(const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
+                                                     const uint16_t* __restrict__ w2, int d, int F,
+                                                     float* __restrict__ scales) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + wave, m = blockIdx.y;
+    if (j >= F) return;
+    const uint16_t* row = (m == 0 ? w0 : (m == 1 ? w1 : w2)) + (size_t)j * d;
+    float amax = 0.f;
+    for (int i = lane; i < d; i += kWave) amax = fmaxf(amax, fabsf(bf16_to_f32(row[i])));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    if (lane == 0) scales[(size_t)m * F + j] = (float)((double)amax / 127.0);
+}
+
+// Codes: grid (ceil(F * d / 8 / 256), 3), block 256; thread = 8 consecutive
+// weights of one row (16 bytes in, 8 bytes out).
+__global__ void __launch_bounds__(256) k_qrow_codes(const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1,
+                                                    const uint16_t* __restrict__ w2, int d, int F,
+                                                    const float* __restrict__ scales, int8_t* __restrict__ codes) {
+    const size_t n8 = (size_t)F * d / 8;
+    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y;
+    if (e >= n8) return;
+    const uint16_t* w = m == 0 ? w0 : (m == 1 ? w1 : w2);
+    const size_t i0 = e * 8;
+    const int j = (int)(i0 / d);
+    const float s = scales[(size_t)m * F + j];
+    const uint4 v = *reinterpret_cast<const uint4*>(w + i0);
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float f = __uint_as_float(k & 1 ? (wd[k >> 1] & 0xffff0000u) : (wd[k >> 1] << 16));
+        out[k >> 2] |= (uint32_t)(quant_code(f, s, 127.f) & 0xff) << (8 * (k & 3));
+    }
+    *reinterpret_cast<uint2*>(codes + (size_t)m * F * d + i0) = make_uint2(out[0], out[1]);
+}
+
+hipError_t launch_build_qweights(const uint16_t* wg_t, const uint16_t* wu_t, const uint16_t* wd, int d, int F,
+                                 int8_t* codes, float* scales, hipStream_t s) {
+    hipLaunchKernelGGL(k_qrow_scales, dim3((F + 3) / 4, 3), dim3(256), 0, s, wg_t, wu_t, wd, d, F, scales);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n8 = (size_t)F * d / 8;
+    hipLaunchKernelGGL(k_qrow_codes, dim3((unsigned)((n8 + 255) / 256), 3), dim3(256), 0, s, wg_t, wu_t, wd, d, F,
+                       scales, codes);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Stage 1.  grid (NB1, B), block 512 (8 waves).
 //
 // Work items: (tile, chunk) pairs, tile-major, chunk = kChunk consecutive entries

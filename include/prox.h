@@ -195,6 +195,44 @@ prox_status prox_ffn_forward_taps(const void* x, int32_t batch, const prox_weigh
                                   uint8_t* mask, int32_t* idx, void* workspace, size_t ws_bytes,
                                   const prox_taps* taps, void* stream);
 
+/* ---- Quantized Stage-2 weights ---------------------------------------------
+ * "Prox: ...", Abstract: the method is compatible with quantization.  Every
+ * row of W_gate^T, W_up^T (the weights of one channel) and W_down (the output
+ * direction of one channel) as int8 codes with one fp32 scale per row, by
+ * the int8 proxy's rule (scale = fp32(max|row| / 127), code =
+ * clamp(round-half-even(fp32(w / scale)), -127, 127)); Stage 2 then streams
+ * d_model bytes per row instead of 2 * d_model.  Stage 1 is unchanged (its
+ * proxy is built from the bf16 weights).
+ * Layout of buf (device): codes gate [d_ff][d_model], up, down (int8), then
+ * at scale_offset fp32 scales gate [d_ff], up [d_ff], down [d_ff].          */
+typedef struct {
+    int32_t d_model;
+    int32_t d_ff;
+    size_t scale_offset;
+    size_t bytes;
+    void* buf;
+} prox_qweights;
+
+/* Bytes of the quantized weights of this shape (d_model % 8 == 0 and the
+ * limits above); 0 if the arguments are invalid. */
+size_t prox_qweights_bytes(int32_t d_model, int32_t d_ff);
+
+/* Quantize w's three bf16 matrices into the caller's device buffer `buf`
+ * (buf_bytes >= prox_qweights_bytes, 256-byte aligned); fills the host
+ * descriptor `out`.  One-time, stream-ordered. */
+prox_status prox_build_qweights(const prox_weights* w, void* buf, size_t buf_bytes, prox_qweights* out,
+                                void* stream);
+
+/* prox_ffn_forward_taps with the Stage-2 rows taken from `q` (int8 rows and
+ * scales): g_j = s_g,j (x . q_g,j), u_j likewise, h_j = silu(g_j) u_j and
+ * y = sum over the kept j of h_j s_d,j q_d,j.  Stage 1 and every other
+ * argument as prox_ffn_forward_taps (taps nullable); the workspace is the one
+ * prox_workspace_bytes gives for the proxy's kind.  The per-token Stage-2
+ * kernel runs for every batch.  PROX_E_UNSUPPORTED for an exact-mode proxy. */
+prox_status prox_ffn_forward_q8(const void* x, int32_t batch, const prox_qweights* q, const prox_proxy* p,
+                                int32_t k_in, int32_t k_ff, float* y, uint8_t* mask, int32_t* idx,
+                                void* workspace, size_t ws_bytes, const prox_taps* taps, void* stream);
+
 /* ---- Allocation-free forward ----------------------------------------------
  * For callers that cannot allocate device memory around a forward (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

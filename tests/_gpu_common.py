@@ -80,6 +80,22 @@ class Case:
         self.weights = P.Weights(to_dev(wg_bits), to_dev(wu_bits), to_dev(wd_bits))
         self.proxy = P.build_proxy(self.weights, kind)
         self._oproxies = None
+        self.gq = None        # quantized Stage-2 weights (GPU), when in use
+        self.oq = None        # the oracle's
+
+    def use_q8(self):
+        """Run Stage 2 on the quantized rows (prox_ffn_forward_q8) from now on."""
+        self.gq = P.build_qweights(self.weights)
+        self.oq = O.build_qweights(self.wg, self.wu, self.wd)
+        return self
+
+    def check_qweights(self):
+        codes, scales = self.gq.codes_and_scales()
+        codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+        for m, (q, s) in enumerate(((self.oq.qg, self.oq.sg), (self.oq.qu, self.oq.su), (self.oq.qd, self.oq.sd))):
+            assert np.array_equal(codes[m], q), f"matrix {m}: codes differ"
+            assert np.array_equal(scales[m].view(np.uint32), s.astype(np.float32).view(np.uint32)), \
+                f"matrix {m}: scales differ"
 
     def oracle_proxies(self):
         if self._oproxies is None:
@@ -95,7 +111,8 @@ class Case:
         assert np.array_equal(su.view(np.uint32), pu.s.astype(np.float32).view(np.uint32)), "up scales differ"
 
     def run_gpu(self, k_in, k_ff, taps=True):
-        out = P.ffn_forward(self.dx, self.weights, self.proxy, k_in, k_ff, taps=taps)
+        out = P.ffn_forward(self.dx, self.gq if self.gq is not None else self.weights, self.proxy, k_in, k_ff,
+                            taps=taps)
         torch.cuda.synchronize()
         return out
 
@@ -113,7 +130,8 @@ class Case:
                  "max_rel_h": 0.0}
         s1 = O.stage1_batch(self.x[toks], pg, pu, k_in, k_ff)
         gms = [np.flatnonzero(mask[b]) for b in toks]
-        _, yrefs = O.stage2_batch(self.x[toks], self.wg, self.wu, self.wd, gms)
+        sw = (self.oq.wg_t, self.oq.wu_t, self.oq.wd) if self.gq is not None else (self.wg, self.wu, self.wd)
+        _, yrefs = O.stage2_batch(self.x[toks], *sw, gms)
         for n, b in enumerate(toks):
             s_in, g_hat, u_hat, h_hat, okey, omask, t = s1[n]
             assert np.array_equal(in_idx[b], s_in), f"{label} token {b}: kept inputs differ"
