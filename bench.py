@@ -39,6 +39,7 @@ from prox_workloads import gen_weights, gen_x, workloads  # noqa: E402
 
 METRIC = "sparse FFN-layer µs/token and achieved HBM GB/s (% peak) at 70% sparsity"
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0
 LLC_BYTES = 256 << 20
 BATCH_MIN = 4   # the library's switch to the matrix-core path (tokens per call)
 
@@ -248,6 +249,16 @@ def main(argv=None):
     else:
         dom_kernel = {0: "k_xsel + k_proxy_batch",
                       1: "k_stage2 (selection) + k_gateup_batch + k_down_batch"}.get(dom, "k_reduce_y")
+    # prefill (more than 64 tokens per call): bound by the matrix cores; the
+    # phase events time only the last 64-token sub-batch, so the roofline
+    # entry is the whole call's algorithmic flops over its step time
+    prefill = B > 64
+    if prefill:
+        flops = 0
+        for layer in range(n_layers):
+            d, F = wl.layers[layer].d, wl.layers[layer].F
+            flops += B * (6 * F * d if args.mode == "dense" else 4 * k_in_of(layer) * F + 6 * wl.k_ff(layer) * d)
+        tflops = flops / (ms_per_step * 1e-3) / 1e12
     src_hash = kernel_sources_hash()
     prof = committed_profile(wl.name, dom_kernel, src_hash, n_layers) if args.mode == "proxy" else {}
     probe = None if args.no_read_probe else read_probe_gbs(P, torch, dev)
@@ -298,6 +309,14 @@ def main(argv=None):
                      "profile": prof.get("file"),
                      "layer_achieved": round(gbs, 1), "layer_frac": round(gbs / PEAK_HBM_GBS, 4)},
         "read_probe_GBps": round(probe, 1) if probe else None,
+        **({"roofline": {"bound": "mfma", "kernel": "whole call: sub-batches of 64 tokens (k_xsel, k_proxy_batch, "
+                                                  "k_stage2 selection, k_gateup_batch, k_down_batch, k_reduce_y)"
+                         if args.mode != "dense" else dom_kernel,
+                         "achieved": round(tflops, 2), "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_MFMA_BF16_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops": int(flops),
+                         "flops_definition": "per token 4*k_in*d_ff (proxy) + 6*k_ff*d_model (Stage 2)"
+                         if args.mode != "dense" else "per token 6*d_ff*d_model"}} if prefill else {}),
         "kernel_sources_sha256": src_hash,
         "library": {"path": os.path.relpath(P.LIB_PATH, ROOT), "sha256": P.library_sha256()},
         "setup_s": round(setup_s, 1),

@@ -116,7 +116,7 @@ extern "C" size_t prox_proxy_bytes(int32_t d, int32_t F, int32_t kind) {
 extern "C" size_t prox_workspace_bytes(int32_t d, int32_t F, int32_t batch, int32_t kind) {
     if (shape_error(d, F, kind) || limit_error(d, F)) return 0;
     if (batch < 1 || batch > PROX_MAX_BATCH) return 0;
-    return ws_layout(d, F, batch, kind).total;
+    return ws_layout(d, F, batch < PROX_CHUNK_BATCH ? batch : PROX_CHUNK_BATCH, kind).total;
 }
 
 extern "C" prox_status prox_build_proxy(const prox_weights* w, int32_t kind, void* buf,
@@ -190,6 +190,40 @@ prox_status forward_impl(const void* x, int32_t batch, int d, int F, const S2Row
     if (!aligned(x, 16) || !aligned(y, 16) || (p->kind != PROX_PROXY_EXACT_BF16 && !aligned(p->buf, 256)))
         return fail(PROX_E_INVALID, "misaligned x, y or proxy");
     if (!aligned(workspace, 256)) return fail(PROX_E_INVALID, "workspace must be 256-byte aligned");
+    if (batch > PROX_CHUNK_BATCH) {
+        // prefill: consecutive sub-batches, each a forward of its own over the
+        // same workspace (stream order keeps them apart); taps per token
+        // follow the sub-batch, the phase events time the last one
+        const WsLayout Lc = ws_layout(d, F, PROX_CHUNK_BATCH, p->kind);
+        if (ws_bytes < Lc.total) return fail(PROX_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, Lc.total);
+        void* const* ev = (taps && taps->events && taps->n_events >= PROX_N_PHASES + 1) ? taps->events : nullptr;
+        if (ev) {
+            hipError_t e = hipEventRecord((hipEvent_t)ev[0], (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "event record");
+        }
+        for (int c0 = 0; c0 < batch; c0 += PROX_CHUNK_BATCH) {
+            const int nb = batch - c0 < PROX_CHUNK_BATCH ? batch - c0 : PROX_CHUNK_BATCH;
+            const bool last = c0 + nb == batch;
+            prox_taps t{};
+            const prox_taps* tp = nullptr;
+            if (taps) {
+                t.in_idx = taps->in_idx ? taps->in_idx + (size_t)c0 * k_in : nullptr;
+                t.key = taps->key ? taps->key + (size_t)c0 * F : nullptr;
+                t.h_hat = taps->h_hat ? taps->h_hat + (size_t)c0 * F : nullptr;
+                t.stream_idx = taps->stream_idx ? taps->stream_idx + (size_t)c0 * k_ff : nullptr;
+                t.events = last ? taps->events : nullptr;
+                t.n_events = last ? taps->n_events : 0;
+                tp = &t;
+            }
+            const prox_status st = forward_impl(static_cast<const uint16_t*>(x) + (size_t)c0 * d, nb, d, F, rows, p,
+                                                k_in, k_ff, y + (size_t)c0 * d,
+                                                mask ? mask + (size_t)c0 * F : nullptr,
+                                                idx ? idx + (size_t)c0 * k_ff : nullptr, workspace, ws_bytes, tp,
+                                                stream);
+            if (st != PROX_OK) return st;
+        }
+        return PROX_OK;
+    }
     const WsLayout L = ws_layout(d, F, batch, p->kind);
     if (ws_bytes < L.total) return fail(PROX_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
 

@@ -66,10 +66,13 @@ typedef enum {
 } prox_proxy_kind;
 
 /* Limits of this build: 8 <= d_model <= 16384, d_model % 8 == 0 (int4: % 128);
- * 1 <= d_ff <= 32768; 1 <= batch <= 64. */
+ * 1 <= d_ff <= 32768; 1 <= batch <= 4096.  Batches above PROX_CHUNK_BATCH
+ * tokens (prefill) run as consecutive sub-batches of at most that many
+ * tokens within the call, sharing one workspace sized for one sub-batch. */
 #define PROX_MAX_D_MODEL 16384
 #define PROX_MAX_D_FF 32768
-#define PROX_MAX_BATCH 64
+#define PROX_MAX_BATCH 4096
+#define PROX_CHUNK_BATCH 64
 
 /* The three bf16 weight matrices of one SwiGLU FFN, all device, all [d_ff][d_model]:
  *   w_gate_t row j = W_gate[:, j]   (the gate weight stored output-major)
@@ -122,7 +125,9 @@ typedef struct {
  * the stream before the first launch and events[p + 1] after phase p.  A phase
  * is one kernel below 4 tokens per call; from 4 tokens stage 1 is the input
  * selection and the proxy GEMM, stage 2 the channel selection, gate/up and
- * down projections.
+ * down projections.  Above PROX_CHUNK_BATCH tokens the events time the last
+ * sub-batch (events[0] is still recorded before the first).  The other taps
+ * cover every token.
  *   stream_idx [batch][k_ff]  below 4 tokens per call only (untouched from 4):
  *          the channels whose rows the Stage-2 blocks actually stream, each
  *          block's list at the ranks of its share; over all blocks a

@@ -13,6 +13,7 @@ Shapes and distributions follow the five workloads the path is measured on:
   c4  70B layer            d=8192, F=28672, B in {1,8},  int8 proxy,  keep 60 %, sparsity 50/70 %
   c5  mixed stack          64 layers alternating (3584, 18944) / (5120, 13824), B=32, int4 g128,
                            keep 60 %, sparsity 80 %
+  c2_p512  prefill         the c2 layer over 512 tokens in one call (sparsity 70 %)
 
 Weights are N(0, 0.02) in fp32 rounded to bf16 (round to nearest even).
 Activations x are Laplace(0, 1) in fp32; c1/c2 scale 4 fixed outlier dims by
@@ -107,6 +108,9 @@ def workloads() -> Dict[str, Workload]:
     s2 = LayerShape(4096, 11008)
     for sp in (50, 70, 90):
         w[f"c2_s{sp}"] = Workload(f"c2_s{sp}", 2, (s2,), 1, "int8", 60, sp, "outlier", 4, 20.0)
+    # prefill: the Llama-2-7B layer over 512 tokens at once (every token its
+    # own mask; the union of the masks covers nearly every channel)
+    w["c2_p512"] = Workload("c2_p512", 2, (s2,), 512, "int8", 60, 70, "outlier", 4, 20.0)
     s3 = LayerShape(4096, 14336)
     for b in (1, 4, 16):
         w[f"c3_b{b}"] = Workload(f"c3_b{b}", 3, _stack([s3], 32), b, "int4", 60, 70, "rmsnorm")

@@ -51,7 +51,9 @@ def test_size_queries_reject_bad_shapes():
     assert P.proxy_bytes(32768, 64, "int8") == 0         # above the d_model limit
     assert _lib.prox_proxy_bytes(512, 64, 7) == 0        # unknown kind
     assert P.workspace_bytes(512, 64, 0, "int8") == 0
-    assert P.workspace_bytes(512, 64, 65, "int8") == 0
+    assert P.workspace_bytes(512, 64, 4097, "int8") == 0
+    # prefill batches share one sub-batch workspace
+    assert P.workspace_bytes(512, 64, 4096, "int8") == P.workspace_bytes(512, 64, 64, "int8")
     assert P.workspace_bytes(4096, 11008, 1, "int8") > 0
 
 
@@ -86,7 +88,7 @@ def test_forward_validation():
     assert _fwd(ws=0) == INVALID
     assert _fwd(w=_weights(null_down=True)) == INVALID
     assert _fwd(B=0) == INVALID
-    assert _fwd(B=65) == UNSUPPORTED
+    assert _fwd(B=4097) == UNSUPPORTED
     assert _fwd(k_in=-1) == INVALID
     assert _fwd(k_in=513) == INVALID
     assert _fwd(k_ff=1377) == INVALID
