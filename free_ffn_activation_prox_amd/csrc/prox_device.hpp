@@ -57,12 +57,39 @@ __device__ __forceinline__ int tile_arrive(unsigned long long* cnt, uint32_t gen
     }
 }
 
-// Measurement hook: thread 0 of the block stores the 100 MHz real-time
-// counter at one of eight points of kernel `kern` (timeline layout
-// [kern][1024 blocks][8 points], block = blockIdx.y * gridDim.x + blockIdx.x).
+// Measurement hook: thread 0 of the block takes the 100 MHz real-time counter
+// at one of eight points of kernel `kern` into LDS, and tl_flush copies the
+// eight stamps to the timeline (layout [kern][1024 blocks][8 points], block =
+// blockIdx.y * gridDim.x + blockIdx.x) when the block ends.  Point 0 clears
+// the others first (a point not reached reads 0).  The stamps go through LDS
+// so that a mark never waits behind the block's own weight loads in the
+// vector memory queue.
+__device__ __forceinline__ unsigned long long* tl_slots() {
+    __shared__ unsigned long long slots[8];
+    return slots;
+}
 __device__ __forceinline__ void tl_mark(unsigned long long* tl, int kern, int point) {
-    if (tl && threadIdx.x == 0)
-        tl[((size_t)kern * 1024 + blockIdx.y * gridDim.x + blockIdx.x) * 8 + point] = __builtin_amdgcn_s_memrealtime();
+    (void)kern;
+    if (tl && threadIdx.x == 0) {
+        if (point == 0)
+            for (int p = 1; p < 8; ++p) tl_slots()[p] = 0ull;
+        tl_slots()[point] = __builtin_amdgcn_s_memrealtime();
+    }
+}
+__device__ __forceinline__ void tl_flush(unsigned long long* tl, int kern) {
+    if (tl && threadIdx.x == 0) {
+        unsigned long long* dst = tl + ((size_t)kern * 1024 + blockIdx.y * gridDim.x + blockIdx.x) * 8;
+        for (int p = 0; p < 8; ++p) dst[p] = tl_slots()[p];
+    }
+}
+
+// floor(w * n / parts) in 32-bit arithmetic (the callers' products stay below
+// 2^32: w <= parts <= 1024 and n < 2^22).  Operands that are uniform over the
+// wave are moved to scalar registers first, so the division runs once per
+// wave on the scalar unit instead of as a 64-lane sequence.
+__device__ __forceinline__ int split_point(int w, int n, int parts) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readfirstlane(w) * (uint32_t)__builtin_amdgcn_readfirstlane(n);
+    return (int)(a / (uint32_t)__builtin_amdgcn_readfirstlane(parts));
 }
 
 // Number of set bits of `m` below this lane.
@@ -367,6 +394,54 @@ __device__ __forceinline__ bool block_hist_bin_regs(const uint32_t (&c)[NB / NT]
     lds_barrier();
     st = SelectState{(uint32_t)sc[20], shift, sc[21], k - sc[21], 0};
     lds_barrier();
+    return true;
+}
+
+// The same from a histogram in LDS (`hist`, NB bins, 16-byte aligned) with
+// the search spread over a wave: thread t sums bins NB - (t + 1) * PER ..
+// NB - t * PER - 1, one block scan finds the thread whose bins hold the k-th
+// largest key, and wave 0 finds the bin among that thread's PER bins with one
+// wave scan (lane j <-> the j-th bin from the top).  No thread walks its bins
+// one by one.  Same outputs and failure rule as block_hist_bin_regs.
+template <int NT, int NB>
+__device__ __forceinline__ bool block_hist_bin_wave(const uint32_t* hist, int k, int n, int shift, int* sc,
+                                                    SelectState& st) {
+    constexpr int PER = NB / NT;
+    static_assert(PER % 4 == 0 && PER <= kWave, "16-byte reads; one lane per bin of a thread");
+    const int t = threadIdx.x;
+    uint32_t mine = 0, mx = 0;
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(hist + NB - (t + 1) * PER);
+#pragma unroll
+        for (int v = 0; v < PER / 4; ++v) {
+            const uint4 u = src[v];
+            mine += u.x + u.y + u.z + u.w;
+            mx = max(max(mx, max(u.x, u.y)), max(u.z, u.w));
+        }
+    }
+    // a bin above n (a histogram that is not this token's) makes the total
+    // differ from n; so does a sum that does not add up
+    int tot;
+    const int cum = block_excl_scan<NT>(mx > (uint32_t)n ? n + 1 : (int)min(mine, (uint32_t)n + 1u), sc, tot);
+    if (tot != n) return false;
+    if (cum < k && k <= cum + (int)mine) {
+        sc[20] = t;
+        sc[21] = cum;
+    }
+    lds_barrier();
+    if (t < kWave) {
+        const int ts = sc[20], cum0 = sc[21];
+        const int bin = NB - 1 - ts * PER - t;
+        const uint32_t cnt = t < PER ? hist[bin] : 0u;
+        const uint32_t incl = wave_incl_scan(cnt);
+        const uint64_t reach = __ballot(cum0 + (int)incl >= k);
+        if (t == (int)__builtin_ctzll(reach)) {
+            sc[22] = bin;
+            sc[23] = cum0 + (int)(incl - cnt);
+        }
+    }
+    lds_barrier();
+    st = SelectState{(uint32_t)sc[22], shift, sc[23], k - sc[23], 0};
     return true;
 }
 

@@ -118,6 +118,7 @@ __global__ void __launch_bounds__(kExThreads) k_exact_h(const uint16_t* __restri
         }
     }
     tl_mark(tl, 0, 3);
+    tl_flush(tl, 0);
 }
 
 hipError_t launch_exact_h(const uint16_t* x, int B, int d, const uint16_t* wg_t, const uint16_t* wu_t, int F,

@@ -13,9 +13,9 @@ constexpr int kMaxW2Total = 512;     // upper bound on Stage-2 blocks per launch
 constexpr int kMaxS1Total = 512;     // upper bound on Stage-1 blocks per launch (all tokens)
 constexpr int kPartChannels = 128;   // channels per partial-sum slot (the int4 tile width)
 // Coarse histogram of the ranking keys that each Stage-2 block builds in LDS
-// for its token: the bin of a key is its fp32 bit pattern >> 18 (keys are
-// >= 0, so 13 bits: sign 0, exponent, 5 mantissa bits; 32 bins per binade).
-constexpr int kGhShift = 18;
+// for its token: the bin of a key is its fp32 bit pattern >> 17 (keys are
+// >= 0, so 14 bits: sign 0, exponent, 6 mantissa bits; 64 bins per binade).
+constexpr int kGhShift = 17;
 constexpr int kGhBins = 1 << (31 - kGhShift);
 // Stage-2 LDS words holding the histogram (and 64 spare bins for keys past
 // F), then (slow paths) every key of F.

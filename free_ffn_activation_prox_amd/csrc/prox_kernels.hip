@@ -231,9 +231,11 @@ constexpr int kSlots = 64;
 // largest w with i0(w) <= i.  The segment of (tile, block) is stored at
 // slot tile + block: along the tile-major item order both never decrease and
 // at least one grows, so the slots are distinct and below tiles + nb1.
-__device__ __host__ __forceinline__ long long s1_item0(int w, long long T, int nb1) { return (long long)w * T / nb1; }
-__device__ __host__ __forceinline__ int s1_block_of(long long i, long long T, int nb1) {
-    return (int)(((i + 1) * nb1 - 1) / T);
+// (32-bit arithmetic: T = tiles * nch <= 512 * 4096 and nb1 <= 512 keep
+// every product below 2^31.)
+__device__ __forceinline__ int s1_item0(int w, int T, int nb1) { return split_point(w, T, nb1); }
+__device__ __forceinline__ int s1_block_of(int i, int T, int nb1) {
+    return (int)(((uint32_t)(i + 1) * (uint32_t)nb1 - 1u) / (uint32_t)T);
 }
 
 
@@ -332,6 +334,7 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
 #pragma unroll
         for (int q = 0; q < PX; ++q) atomicAdd(&hist[key[q] >= 0 ? (key[q] >> 4) : 2048 + 16], 1u);
         lds_barrier();
+        tl_mark(a.tl, 0, 4);
         uint32_t tb;
         static_assert(NT * 4 == 2048, "one 16-byte read of 4 bins per thread");
         find_bin4<NT>(hist, k_in, sc, tb, cgt);
@@ -361,6 +364,7 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         }
         cgt = cum;                                         // keys > T
     }
+    tl_mark(a.tl, 0, 5);
     const int need = all ? 0 : k_in - cgt;                 // keys equal to T to keep
     int gt = 0, eq = 0;
 #pragma unroll
@@ -398,6 +402,7 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         na += on[q] && big ? 1 : 0;
     }
     uint32_t tot2;
+    tl_mark(a.tl, 0, 6);
     const uint32_t pre2 = block_excl_scan_u32<NT>(((uint32_t)nb << 16) | (uint32_t)na, sc, tot2);
     if (k_in > 0) {
         int pb = (int)(pre2 >> 16), pa = (int)((uint32_t)tot2 >> 16) + (int)(pre2 & 0xffffu);
@@ -584,16 +589,16 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     tl_mark(a.tl, 0, 1);
     bool flags_done = false;     // the chunk flags are computed under the block's first loads
 
-    const long long T = (long long)a.tiles * nch;
-    const long long i0 = s1_item0(wb, T, a.nb1), i1 = s1_item0(wb + 1, T, a.nb1);
+    const int T = a.tiles * nch;
+    const int i0 = s1_item0(wb, T, a.nb1), i1 = s1_item0(wb + 1, T, a.nb1);
     const int slot = w * 8 + (l >> 3);
     const int cb = l & 7;
     const uint32_t codes_bytes = (uint32_t)a.tiles * (uint32_t)d * (uint32_t)kTileRowBytes;
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.p.codes, codes_bytes);
     const uint32_t lane_off = (uint32_t)cb * 16u;
-    for (int tile = (int)(i0 / nch); (long long)tile * nch < i1; ++tile) {
-        const int ca = (int)(max(i0, (long long)tile * nch) - (long long)tile * nch);
-        const int ce = (int)(min(i1, (long long)(tile + 1) * nch) - (long long)tile * nch);
+    for (int tile = i0 / nch; tile * nch < i1; ++tile) {
+        const int ca = max(i0, tile * nch) - tile * nch;
+        const int ce = min(i1, (tile + 1) * nch) - tile * nch;
         const uint32_t tile_off = (uint32_t)tile * (uint32_t)d * (uint32_t)kTileRowBytes;
         // int8 channel scales, requested now and used after the stream
         float sgj = 0.f, suj = 0.f;
@@ -641,8 +646,9 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
             // share their 128-row group, so the group scales are applied (and
             // loaded) once per group change instead of once per chunk
             const int n = ce - ca;
-            const int cs0 = ca + (int)((long long)slot * n / kSlots);
-            const int cs1 = ca + (int)((long long)(slot + 1) * n / kSlots);
+            // (slot differs between lanes; kSlots is a power of two)
+            const int cs0 = ca + (int)((uint32_t)(slot * n) / (uint32_t)kSlots);
+            const int cs1 = ca + (int)((uint32_t)((slot + 1) * n) / (uint32_t)kSlots);
             load_chunk(list, xflags, k_in, cs0, cs1, crs, codes_bytes, tile_off, lane_off, c0);
             if (!flags_done) {
                 stage1_flags(list, k_in);
@@ -688,8 +694,8 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) v += red[q][t / TC][t % TC];
         }
-        const int w0 = s1_block_of((long long)tile * nch, T, a.nb1);
-        const int w1 = s1_block_of((long long)(tile + 1) * nch - 1, T, a.nb1);
+        const int w0 = s1_block_of(tile * nch, T, a.nb1);
+        const int w1 = s1_block_of((tile + 1) * nch - 1, T, a.nb1);
         bool last = true;
         if (w1 > w0) {
             // the tile is split: publish this segment, and the block that
@@ -721,6 +727,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         lds_barrier();   // `red` and `gsum` are rewritten by the next tile
     }
     tl_mark(a.tl, 0, 3);
+    tl_flush(a.tl, 0);
 }
 
 template <int KIND, int PX>
@@ -972,14 +979,16 @@ __device__ __forceinline__ void consume_group(const RowGroup<MODE, R, G>& rg, co
 // ---------------------------------------------------------------------------
 // Stage 2 top-k.  A threshold bin (prefix at shift) splits the keys: those in
 // higher bins are kept for certain ("certain"), those in the bin are
-// "candidates".  The bin comes from a histogram of the keys' top 13 bits that
+// "candidates".  The bin comes from a histogram of the keys' top 14 bits that
 // the block builds in LDS (should its bins not add up, from a radix digit of
 // the block's own keys).  Thread t owns channels t*PK .. t*PK + PK - 1 for the
 // block-wide counts; the candidates go to LDS in index order and each gets
 // its rank (key descending, index ascending), so a candidate is kept when its
-// rank is below k - (certain keys).  The block's own range is handled one
-// channel per thread: its certain channels are listed and their first rows
-// requested as soon as the bin is known, before the candidates are resolved.
+// rank is below k - (certain keys).  Up to 64 candidates (the usual case: 64
+// bins per binade leave a few dozen keys in the threshold bin) are ranked by
+// one wave; more take block-wide passes.  The block's certain channels are
+// listed and their first rows requested as soon as the bin is known, before
+// the candidates are resolved.
 //
 // The list: certain channels of the range in index order, then its kept
 // candidates in index order.  The first group holds the leading E = min(nc, G)
@@ -1001,11 +1010,12 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     __shared__ int sc[24];
     __shared__ int wc[4][NW];
     __shared__ float red[2][NW * 2 * G];
+    __shared__ uint16_t chan_sink[kWave];                // stores of keys that list nothing
 
     tl_mark(a.tl, 1, 0);
     const int w = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int F = a.F, k = a.k, W2 = a.W2;
-    const int r0 = (int)((long long)w * F / W2), r1 = (int)((long long)(w + 1) * F / W2);
+    const int r0 = split_point(w, F, W2), r1 = split_point(w + 1, F, W2);
     const int L = r1 - r0;                                 // channels of this block's range
     uint32_t* keys = dyn2;                                 // [s2_keys_words(F)] the key histogram, then every key (index order)
     uint32_t* cval = keys + s2_keys_words(F);              // [kCandCap + 64] candidate keys, index order
@@ -1072,17 +1082,9 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 #pragma unroll
         for (int q = 0; q < PK; ++q) atomicAdd(&keys[min(kb[q] >> kGhShift, (uint32_t)(kGhBins + 63))], 1u);
         lds_barrier();
-        uint32_t cbin[kGhBins / NT];
-        {
-            const uint4* src = reinterpret_cast<const uint4*>(keys + kGhBins - (t + 1) * (kGhBins / NT));
-#pragma unroll
-            for (int v = 0; v < kGhBins / NT / 4; ++v) {
-                const uint4 u = src[v];
-                cbin[4 * v] = u.x; cbin[4 * v + 1] = u.y; cbin[4 * v + 2] = u.z; cbin[4 * v + 3] = u.w;
-            }
-        }
+        tl_mark(a.tl, 1, 4);
         // (the scans below hold barriers before keys_to_lds overwrites the histogram)
-        if (!block_hist_bin_regs<NT, kGhBins>(cbin, k, F, kGhShift, sc, st)) {
+        if (!block_hist_bin_wave<NT, kGhBins>(keys, k, F, kGhShift, sc, st)) {
             bool valid[PK];
 #pragma unroll
             for (int q = 0; q < PK; ++q) valid[q] = (int)kb[q] >= 0;
@@ -1113,30 +1115,37 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int ncand = (int)((uint32_t)tot & 0xffffu);
     const int C = (int)((uint32_t)tot >> 16);            // certain keys in all
     const int crank0 = (int)(pre >> 16), cp0 = (int)(pre & 0xffffu);
+    tl_mark(a.tl, 1, 5);
     const bool listed = ncand <= kCandCap;                // candidates compacted (else the slow path)
     if (!listed || ncand > kSmallCand) keys_to_lds();     // the slow paths read every key from LDS
     // this block's share of the certain keys: ranks [c0, c1)
-    const int c0 = (int)((long long)w * C / W2), c1 = (int)((long long)(w + 1) * C / W2);
+    const int c0 = split_point(w, C, W2), c1 = split_point(w + 1, C, W2);
     int nc = listed ? c1 - c0 : 0;
     if (listed) {
         // share: the certain keys of rank [c0, c1) into chan; candidates
-        // (index order) into cidx; each lane walks only its set bits
-        if (crank0 < c1 && crank0 + ncert_t > c0) {
-            uint64_t m = cem;
+        // (index order) into cidx / cval.  Every key of the thread takes one
+        // store, to its slot or to a per-lane sink past the arrays' ends, so
+        // the loops have no branches.
+        const int lane = t & (kWave - 1);
+        if (STREAM && crank0 < c1 && crank0 + ncert_t > c0) {
             int cr = crank0;
-            while (m) {
-                const int q = __builtin_ctzll(m);
-                m &= m - 1;
-                if (STREAM && cr >= c0 && cr < c1) chan[cr - c0] = (uint16_t)(t * PK + q);
-                ++cr;
+#pragma unroll
+            for (int q = 0; q < PK; ++q) {
+                const bool c = (cem >> q) & 1ull;
+                const bool on = c && cr >= c0 && cr < c1;
+                *(on ? chan + (cr - c0) : chan_sink + lane) = (uint16_t)(t * PK + q);
+                cr += c ? 1 : 0;
             }
         }
-        int cp = cp0;
+        if (nd > 0) {
+            int cp = cp0;
 #pragma unroll
-        for (int q = 0; q < PK; ++q) {
-            if ((cdm >> q) & 1ull) {
-                cidx[cp] = (uint16_t)(t * PK + q);
-                cval[cp++] = kb[q];
+            for (int q = 0; q < PK; ++q) {
+                const bool on = (cdm >> q) & 1ull;
+                const int i = on ? cp : kCandCap + lane;
+                cidx[i] = (uint16_t)(t * PK + q);
+                cval[i] = kb[q];
+                cp += on ? 1 : 0;
             }
         }
     }
@@ -1147,6 +1156,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         sc[18] = crank0 + __popcll(cem & lo);
     }
     lds_barrier();
+    tl_mark(a.tl, 1, 6);
     const int cs = sc[16];                                 // candidates before the range
     const int cert_before = sc[18];                        // certain keys before the range
     const int E = min(nc, G);
@@ -1154,7 +1164,41 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     if constexpr (STREAM) load_group<SM, R, G>(rs, aux, chan, 0, E, row_bytes, mat_bytes, voff, cur);
 
     int nks = 0, kc_before = 0, s0k = 0;
-    if (listed) {
+    if (listed && ncand <= kWave) {
+        // ---- few candidates (the usual case): wave 0 ranks them (key
+        // descending, index ascending), keeps the first k - C, and lists the
+        // block's share of the kept ones; one barrier publishes the counts
+        if (t < kWave) {
+            const bool has = t < ncand;
+            const uint32_t v = has ? cval[t] : 0u;
+            int rank = 0;
+            for (int i = 0; i < ncand; ++i) {
+                const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
+                rank += (u > v || (u == v && i < t)) ? 1 : 0;
+            }
+            const bool kept = has && rank < st.krem;
+            const uint64_t km = __ballot(kept);
+            const int kcount = __popcll(km);
+            const int s0 = split_point(w, kcount, W2), s1 = split_point(w + 1, kcount, W2);
+            const int r = lanes_below(km);                 // rank among the kept, index order
+            if (kept) {
+                const uint16_t j = cidx[t];
+                cidx[t] = (uint16_t)(j | 0x8000u);
+                if (STREAM && r >= s0 && r < s1) chan[nc + r - s0] = j;
+            }
+            if (t == 0) {
+                sc[12] = kcount;
+                sc[13] = __popcll(km & (cs >= 64 ? ~0ull : ((1ull << cs) - 1)));
+            }
+        }
+        lds_barrier();
+        const int KC = sc[12];
+        kc_before = sc[13];
+        const int s0 = split_point(w, KC, W2), s1 = split_point(w + 1, KC, W2);
+        nks = s1 - s0;
+        s0k = s0;
+        tl_mark(a.tl, 1, 7);
+    } else if (listed) {
         // ---- resolve the candidates while those loads are in flight:
         // cidx[i] gets bit 15 when kept
         if (ncand > 0) {
@@ -1217,7 +1261,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             kc_before += tt[1];
         }
         const int KC = run;
-        const int s0 = (int)((long long)w * KC / W2), s1 = (int)((long long)(w + 1) * KC / W2);
+        const int s0 = split_point(w, KC, W2), s1 = split_point(w + 1, KC, W2);
         nks = s1 - s0;
         s0k = s0;
         for (int i = t; i < ncand; i += NT) {
@@ -1244,7 +1288,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         const uint32_t pk = block_excl_scan_u32<NT>(((uint32_t)gt << 16) | (uint32_t)eq, sc, tk);
         int eb = (int)(pk & 0xffffu);
         int pos = (int)(pk >> 16) + min(eb, need);
-        const int k0 = (int)((long long)w * k / W2), k1 = (int)((long long)(w + 1) * k / W2);
+        const int k0 = split_point(w, k, W2), k1 = split_point(w + 1, k, W2);
 #pragma unroll
         for (int q = 0; q < PK; ++q) {
             const bool e = kb[q] == T;
@@ -1289,13 +1333,14 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     lds_barrier();
     if constexpr (!STREAM) {         // selection only: mask and idx are written
         write_range();
+        tl_flush(a.tl, 1);
         return;
     }
     if (a.stream_tap) {
         // the streamed list, at the ranks of the block's shares: certain keys
         // [c0, c1), then kept candidates at C + [s0, s1) (slow path: kept ranks
         // [k0, k1)); over all blocks, a permutation of the token's idx
-        const int base1 = listed ? c0 : (int)((long long)w * k / W2);
+        const int base1 = listed ? c0 : split_point(w, k, W2);
         for (int i = t; i < n; i += NT)
             a.stream_tap[(size_t)b * k + (i < nc ? base1 + i : C + s0k + (i - nc))] = chan[i];
     }
@@ -1353,6 +1398,7 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         }
     }
     tl_mark(a.tl, 1, 3);
+    tl_flush(a.tl, 1);
 }
 
 template <int PK, int R, int G, int MODE>
