@@ -225,6 +225,10 @@ constexpr int kS1Threads = 512;
 // byte flags of the chunks after the kept-input list (k_in + 64 words) in the
 // dynamic LDS: word offset
 __host__ __device__ __forceinline__ int s1_flags_off(int k_in) { return (k_in + 64 + 3) & ~3; }
+// int4: the group table after the flags, 16-byte aligned (word offset)
+__host__ __device__ __forceinline__ int s1_table_off(int k_in) {
+    return (s1_flags_off(k_in) + ((k_in + 3) / 4 + 16 + 3) / 4 + 3) & ~3;
+}
 constexpr int kSlots = 64;
 
 // Items [i0, i1) of block w: i0 = w * T / nb1.  The block holding item i is the
@@ -306,12 +310,15 @@ __device__ __forceinline__ bool chunk_exact32(const Chunk& c) {
     return ok && hi - lo <= 5;
 }
 
-// Input selection.  Fills `list` with the k_in kept inputs in index order.
-// Keys are 15 bits: a 2048-bin histogram of key >> 4 finds the threshold bin,
-// a 16-bin histogram of the low 4 bits of the keys in that bin finds the
-// threshold T itself (every thread scans those 16 bins), and one packed scan
-// of (keys > T, keys == T) places every kept input, the first k_in - #(> T)
-// keys equal to T in index order.  LDS: hist >= 2048 + 16 + 64 words.
+// Input selection.  Fills `list` with the k_in kept inputs: band B (exponent
+// within e_lo .. e_lo + 5, e_lo = the threshold's exponent, not subnormal)
+// first, then band A (the rest), each in index order; sc[16] = the band-B
+// count, sc[17] = max(e_lo, 1).  Keys are 15 bits: a 2048-bin histogram of
+// key >> 4 finds the threshold bin, a 16-bin histogram of the low 4 bits of
+// the keys in that bin finds the threshold T itself (every thread scans those
+// 16 bins), and one packed scan of (keys > T, keys == T) places every kept
+// input, the first k_in - #(> T) keys equal to T in index order.  LDS: hist
+// >= 2048 + 16 + 64 words.
 template <int PX>
 __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32_t* list, uint32_t* hist, int* sc) {
     constexpr int NT = kS1Threads;
@@ -393,11 +400,28 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
             pos += on[q] ? 1 : 0;
         }
     }
-    const int e_hi = all ? 255 : ((T >> 7) & 0xff) + 5;    // keep-all: one band
+    // e_lo: the threshold's exponent (keep-all: the smallest exponent of a
+    // normal input); band B = exponents e_lo .. e_lo + 5, band A = larger
+    // exponents and subnormal inputs
+    int e_lo = (T >> 7) & 0xff;
+    if (all) {
+        int m = 0;
+#pragma unroll
+        for (int q = 0; q < PX; ++q) {
+            const int e = (key[q] >> 7) & 0xff;
+            m = key[q] > 0 && e > 0 ? max(m, 255 - e) : m;
+        }
+        e_lo = 255 - block_max<NT>(m, sc);
+    }
+    const int e_hi = e_lo + 5;
+    auto band_a = [&](int kq) {
+        const int e = (kq >> 7) & 0xff;
+        return e > e_hi || (e == 0 && (kq & 0x7f) != 0);
+    };
     int nb = 0, na = 0;
 #pragma unroll
     for (int q = 0; q < PX; ++q) {
-        const bool big = ((key[q] >> 7) & 0xff) > e_hi;
+        const bool big = band_a(key[q]);
         nb += on[q] && !big ? 1 : 0;
         na += on[q] && big ? 1 : 0;
     }
@@ -409,11 +433,15 @@ __device__ __forceinline__ void stage1_select(const Stage1Args& a, int b, uint32
         uint32_t* dummy = list + k_in + lane;              // lanes with nothing to write
 #pragma unroll
         for (int q = 0; q < PX; ++q) {
-            const bool big = ((key[q] >> 7) & 0xff) > e_hi;
+            const bool big = band_a(key[q]);
             *(on[q] ? list + (big ? pa : pb) : dummy) = ((uint32_t)(t * PX + q) << 16) | raw[q];
             pb += on[q] && !big ? 1 : 0;
             pa += on[q] && big ? 1 : 0;
         }
+    }
+    if (t == 0) {
+        sc[16] = (int)(tot2 >> 16);                        // band-B entries (the list's first ones)
+        sc[17] = max(e_lo, 1);                             // band B's unit exponent
     }
     lds_barrier();
 }
@@ -561,6 +589,205 @@ __device__ __forceinline__ void consume_chunk_i4(const Chunk& c, const float* sg
     }
 }
 
+// ---------------------------------------------------------------------------
+// int4 tile segment: kept-list entries [e0, e1) of one 128-channel tile.
+//
+// Band-B entries (the list's first nbB, index order): 16 lanes per kept row,
+// lane (block bk, matrix m) reading the 8 bytes that hold the 16 codes of
+// matrix m for channels 16 bk .. 16 bk + 15; a slot of 16 lanes streams a
+// contiguous run of the segment's rows with kI4Ring rows in flight.  With
+// every nibble flipped by 8 a code reads as q + 8 in 0..15, the nibbles split
+// into bytes convert with one instruction each, and sum x q = sum x (q + 8) -
+// 8 sum x.  Band-B inputs lie in the six binades e_u .. e_u + 5, so in units
+// of 2^(e_u - 134) every x is an integer below 2^13, every x (q + 8) below
+// 2^17 and every sum over one 128-row group below 2^24: the fp32 sums are
+// exact.  When its run leaves a group a lane turns its sums into integers in
+// those units and adds them to the group's row of an LDS table (integer adds:
+// exact in any order).  After the stream thread t < 256 (matrix t / 128,
+// channel t % 128) forms the sum over groups of s_group times the table entry
+// in fp64, groups in ascending order.  The table holds kI4Win groups; a
+// segment spanning more is taken kI4Win groups at a time.
+//
+// Band-A entries (larger or subnormal inputs, few) are summed in fp64 by the
+// same 256 threads, x q exact in fp32 times the group scale, in list order.
+// Returns, for t < 256, the segment's sum for the thread's (matrix, channel).
+// ---------------------------------------------------------------------------
+constexpr int kI4Ring = 8;
+constexpr int kI4Win = 32;
+constexpr int kI4TableWords = kI4Win * 256;
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    return make_uint2(v.x, v.y);
+}
+
+// First entry in [lo, hi) whose row lies in group >= g (entries ascending).
+__device__ __forceinline__ int i4_group_start(const uint32_t* list, int lo, int hi, int g) {
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)(list[mid] >> 23) < g) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void i4_flush(float (&pg)[16], float& sx, int gw, int m, int bk, int eu, int* table) {
+    if (gw >= 0 && gw < kI4Win) {
+        int* row = table + gw * 256 + m * 128 + 16 * bk;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) atomicAdd(row + c, (int)ldexpf(pg[c] - 8.f * sx, 134 - eu));
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) pg[c] = 0.f;
+    sx = 0.f;
+}
+
+template <int NT>
+__device__ __forceinline__ double i4_segment(const Stage1Args& a, const uint32_t* list, int e0, int e1, int nbB,
+                                             int eu, int tile, __amdgpu_buffer_rsrc_t crs, uint32_t codes_bytes,
+                                             uint32_t tile_off, int* table) {
+    constexpr int NS = NT / 16;                     // slots
+    const int t = threadIdx.x;
+    const int slot = t >> 4, bk = (t & 15) >> 1, m = t & 1;
+    const uint32_t lane_off = (uint32_t)(bk * 16 + m * 8);
+    const int f_pad = a.p.f_pad, groups = a.p.groups;
+    const int tm = (t >> 7) & 1, tc = t & 127;      // the (matrix, channel) of thread t < 256
+    const float* srow = a.p.scales + (size_t)tm * groups * f_pad + (size_t)tile * 128 + tc;
+
+    // ---- band A, eight rows at a time (every load of a batch in flight)
+    double acc_a = 0.0;
+    const int a0 = max(e0, nbB), a1 = e1;
+    if (t < 256) {
+        const uint32_t word_off = (uint32_t)((tc >> 4) * 16 + tm * 8 + ((tc & 15) >> 3) * 4);
+        for (int r0 = a0; r0 < a1; r0 += 8) {
+            uint32_t wd[8];
+            float sv[8], xv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = r0 + j;
+                const bool ok = r < a1;
+                const uint32_t e = ok ? list[r] : 0u;
+                const int i = (int)(e >> 16);
+                wd[j] = buf_load4(crs, ok ? (uint32_t)i * (uint32_t)kTileRowBytes + word_off : codes_bytes, tile_off);
+                sv[j] = ok ? srow[(size_t)(i >> 7) * f_pad] : 0.f;
+                xv[j] = __uint_as_float(e << 16);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc_a = fma((double)(xv[j] * (float)sext4(wd[j], tc & 7)), (double)sv[j], acc_a);
+        }
+    }
+
+    // ---- band B
+    double acc = 0.0;
+    const int b0 = e0, b1 = max(e0, min(e1, nbB));
+    if (b1 > b0) {
+        const int gfirst = (int)(list[b0] >> 23), glast = (int)(list[b1 - 1] >> 23);
+        for (int G0 = gfirst; G0 <= glast; G0 += kI4Win) {
+            for (int i = t; i < kI4TableWords; i += NT) table[i] = 0;
+            const int w0 = G0 > gfirst ? i4_group_start(list, b0, b1, G0) : b0;
+            const int w1 = G0 + kI4Win <= glast ? i4_group_start(list, w0, b1, G0 + kI4Win) : b1;
+            // this window's scales, needed after the stream (unconditional
+            // loads: a group past the last one re-reads the last, and its
+            // table entries are zero)
+            float sw[kI4Win];
+#pragma unroll
+            for (int gw = 0; gw < kI4Win; ++gw) sw[gw] = srow[(size_t)min(G0 + gw, groups - 1) * f_pad];
+            lds_barrier();                          // the table is clear
+            const int n = w1 - w0;
+            const int r0 = w0 + (int)((uint32_t)(slot * n) / (uint32_t)NS);      // this slot's run
+            const int r1 = w0 + (int)((uint32_t)((slot + 1) * n) / (uint32_t)NS);
+            // ring of kI4Ring rows: row r + kI4Ring is requested into the
+            // slot of row r right after row r is consumed; the entries of the
+            // next kI4Ring rows are read while the current ones are consumed
+            // (two entry arrays, alternating).  Rows past the run have entry 0:
+            // they read as x = 0 at an offset past the codes (zeros, no memory
+            // access), so the loads are unconditional.
+            auto entries = [&](int r, uint32_t (&en)[kI4Ring]) {
+#pragma unroll
+                for (int j = 0; j < kI4Ring; ++j) {
+                    const int i = r + j;
+                    const uint32_t e = list[min(i, r1)];     // r1 <= k_in: inside the list
+                    en[j] = i < r1 ? e : 0u;
+                }
+            };
+            auto request = [&](uint32_t e) {
+                return buf_load8(crs, e != 0u ? (e >> 16) * (uint32_t)kTileRowBytes + lane_off : codes_bytes,
+                                 tile_off);
+            };
+            float pg[16], sx = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) pg[c] = 0.f;
+            int cur = r0 < r1 ? (int)(list[r0] >> 23) : G0;
+            auto consume = [&](uint2 v, uint32_t e) {
+                const float x = __uint_as_float(e << 16);
+                const uint32_t wd[2] = {v.x, v.y};             // channels 0..7, 8..15
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    // nibbles flipped by 8 and split into bytes; the opaque
+                    // moves keep each byte's conversion a single instruction
+                    uint32_t lo = (wd[k] ^ 0x88888888u) & 0x0f0f0f0fu, hi = ((wd[k] >> 4) ^ 0x08888888u) & 0x0f0f0f0fu;
+                    asm volatile("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        pg[8 * k + 2 * q] = fmaf(x, ubyte_f(lo, q), pg[8 * k + 2 * q]);
+                        pg[8 * k + 2 * q + 1] = fmaf(x, ubyte_f(hi, q), pg[8 * k + 2 * q + 1]);
+                    }
+                }
+                sx += x;
+                // the sums are final before the slot is reloaded, so the new
+                // load can take the old registers
+#pragma unroll
+                for (int c = 0; c < 16; ++c) asm volatile("" : "+v"(pg[c]));
+            };
+            // one ring's worth of rows.  A row past the run (entry 0, group 0)
+            // may flush the run's sums one row early and leave the lane on
+            // group 0 with zero sums: harmless.  The branch holds no loads, so
+            // the ring's loads stay in flight across it.
+            auto half = [&](uint2 (&bv)[kI4Ring], const uint32_t (&ec)[kI4Ring], const uint32_t (&en)[kI4Ring]) {
+#pragma unroll
+                for (int j = 0; j < kI4Ring; ++j) {
+                    const int g = (int)(ec[j] >> 23);
+                    if (g != cur) {
+                        i4_flush(pg, sx, cur - G0, m, bk, eu, table);
+                        cur = g;
+                    }
+                    consume(bv[j], ec[j]);
+                    bv[j] = request(en[j]);
+                }
+            };
+            uint2 bv[kI4Ring];
+            uint32_t ea[kI4Ring];
+            entries(r0, ea);
+#pragma unroll
+            for (int j = 0; j < kI4Ring; ++j) {
+                bv[j] = request(ea[j]);
+                __builtin_amdgcn_sched_barrier(0);   // issue order = consumption order
+            }
+            for (int r = r0; r < r1; r += kI4Ring) {
+                uint32_t eb[kI4Ring];
+                entries(r + kI4Ring, eb);
+                half(bv, ea, eb);
+#pragma unroll
+                for (int j = 0; j < kI4Ring; ++j) ea[j] = eb[j];
+            }
+            i4_flush(pg, sx, cur - G0, m, bk, eu, table);
+            lds_barrier();                          // the table is complete
+            if (t < 256) {
+                double ws = 0.0;
+#pragma unroll
+                for (int gw = 0; gw < kI4Win; ++gw) ws = fma((double)table[gw * 256 + t], (double)sw[gw], ws);
+                acc += ws;
+            }
+            lds_barrier();                          // read before the next window clears it
+        }
+    }
+    return ldexp(acc, eu - 134) + acc_a;
+}
+
 template <int N>
 __device__ __forceinline__ void settle_d(double (&v)[N]) {
 #pragma unroll
@@ -584,6 +811,7 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
     const int k_in = a.k_in, d = a.d, nch = a.nch;
     uint32_t* list = dyn;                         // [k_in + 64], then the chunks' exactness flags
     const uint8_t* xflags = reinterpret_cast<const uint8_t*>(dyn + s1_flags_off(k_in));
+    int* i4_table = reinterpret_cast<int*>(dyn + s1_table_off(k_in));   // int4: [kI4Win][256]
     tl_mark(a.tl, 0, 0);
     stage1_select<PX>(a, b, list, hist, sc);
     tl_mark(a.tl, 0, 1);
@@ -600,9 +828,16 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         const int ca = max(i0, tile * nch) - tile * nch;
         const int ce = min(i1, (tile + 1) * nch) - tile * nch;
         const uint32_t tile_off = (uint32_t)tile * (uint32_t)d * (uint32_t)kTileRowBytes;
-        // int8 channel scales, requested now and used after the stream
+        // this segment's sums: thread t < 2 TC holds channel t % TC, gate (t < TC) or up
+        double v = 0.0;
         float sgj = 0.f, suj = 0.f;
-        if constexpr (KIND == 1) {
+        if constexpr (KIND == 2) {
+            v = i4_segment<kS1Threads>(a, list, ca * kChunk, min(ce * kChunk, k_in), sc[16], sc[17], tile, crs,
+                                       codes_bytes, tile_off, i4_table);
+            tl_mark(a.tl, 0, 2);
+        } else {
+        // int8 channel scales, requested now and used after the stream
+        {
             const int j = tile * TC + (t % TC);             // < f_pad: always readable
             sgj = a.p.scales[j];
             suj = a.p.scales[(size_t)a.p.f_pad + j];
@@ -614,61 +849,22 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         // chunks ca + slot, + 64, ...: two chunks in flight per slot; the loop
         // has no exit from its middle and its loads are unconditional
         Chunk c0, c1;
-        if constexpr (KIND == 1) {
-            load_chunk(list, xflags, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
-            if (!flags_done) {
-                stage1_flags(list, k_in);
-                lds_barrier();
-                flags_done = true;
-                c0.exact = ca + slot < ce ? xflags[ca + slot] != 0 : true;
-            }
-            for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
-                load_chunk(list, xflags, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
-                consume_chunk_i8(c0, ag, au);
-                settle_d(ag);
-                settle_d(au);
-                load_chunk(list, xflags, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
-                consume_chunk_i8(c1, ag, au);
-                settle_d(ag);
-                settle_d(au);
-            }
-        } else {
-            const float* sgp = a.p.scales + (size_t)tile * TC + cb * 16;
-            const float* sup = sgp + (size_t)a.p.groups * a.p.f_pad;
-            double og[NV], ou[NV];
-#pragma unroll
-            for (int c = 0; c < NV; ++c) og[c] = ou[c] = 0.0;
-            I4State st;
-            st.cur = -1;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) st.sg[q] = st.su[q] = 0.f;
-            // each slot takes a contiguous run of chunks: consecutive kept rows
-            // share their 128-row group, so the group scales are applied (and
-            // loaded) once per group change instead of once per chunk
-            const int n = ce - ca;
-            // (slot differs between lanes; kSlots is a power of two)
-            const int cs0 = ca + (int)((uint32_t)(slot * n) / (uint32_t)kSlots);
-            const int cs1 = ca + (int)((uint32_t)((slot + 1) * n) / (uint32_t)kSlots);
-            load_chunk(list, xflags, k_in, cs0, cs1, crs, codes_bytes, tile_off, lane_off, c0);
-            if (!flags_done) {
-                stage1_flags(list, k_in);
-                lds_barrier();
-                flags_done = true;
-                c0.exact = cs0 < cs1 ? xflags[cs0] != 0 : true;
-            }
-            for (int ch = cs0; ch < cs1; ch += 2) {
-                load_chunk(list, xflags, k_in, ch + 1, cs1, crs, codes_bytes, tile_off, lane_off, c1);
-                consume_chunk_i4(c0, sgp, sup, a.p.f_pad, st, og, ou);
-                settle_d(og);
-                load_chunk(list, xflags, k_in, ch + 2, cs1, crs, codes_bytes, tile_off, lane_off, c0);
-                consume_chunk_i4(c1, sgp, sup, a.p.f_pad, st, og, ou);
-                settle_d(og);
-            }
-#pragma unroll
-            for (int c = 0; c < NV; ++c) {
-                ag[c] = og[c];
-                au[c] = ou[c];
-            }
+        load_chunk(list, xflags, k_in, ca + slot, ce, crs, codes_bytes, tile_off, lane_off, c0);
+        if (!flags_done) {
+            stage1_flags(list, k_in);
+            lds_barrier();
+            flags_done = true;
+            c0.exact = ca + slot < ce ? xflags[ca + slot] != 0 : true;
+        }
+        for (int ch = ca + slot; ch < ce; ch += 2 * kSlots) {
+            load_chunk(list, xflags, k_in, ch + kSlots, ce, crs, codes_bytes, tile_off, lane_off, c1);
+            consume_chunk_i8(c0, ag, au);
+            settle_d(ag);
+            settle_d(au);
+            load_chunk(list, xflags, k_in, ch + 2 * kSlots, ce, crs, codes_bytes, tile_off, lane_off, c0);
+            consume_chunk_i8(c1, ag, au);
+            settle_d(ag);
+            settle_d(au);
         }
         tl_mark(a.tl, 0, 2);
         // reduce the 8 row slots of the wave (lanes l ^ 8, l ^ 16, l ^ 32 share the
@@ -688,11 +884,10 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
             }
         }
         lds_barrier();
-        // this segment's sums: thread t < 2 TC holds channel t % TC, gate (t < TC) or up
-        double v = 0.0;
         if (t < 2 * TC) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) v += red[q][t / TC][t % TC];
+        }
         }
         const int w0 = s1_block_of(tile * nch, T, a.nb1);
         const int w1 = s1_block_of((tile + 1) * nch - 1, T, a.nb1);
@@ -732,7 +927,8 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
 
 template <int KIND, int PX>
 static hipError_t go_stage1(const Stage1Args& a, int B, hipStream_t s) {
-    const size_t dyn = (size_t)s1_flags_off(a.k_in) * 4 + (size_t)((a.k_in + kChunk - 1) / kChunk + 16);
+    const size_t dyn = KIND == 2 ? ((size_t)s1_table_off(a.k_in) + kI4TableWords) * 4
+                                 : (size_t)s1_flags_off(a.k_in) * 4 + (size_t)((a.k_in + kChunk - 1) / kChunk + 16);
     auto fn = k_stage1<KIND, PX>;
     if (dyn > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
@@ -828,10 +1024,6 @@ struct RowAux {
     const float* sd;
 };
 
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
-    return make_uint2(v.x, v.y);
-}
 
 template <int MODE, int R, int G>
 __device__ __forceinline__ void load_group(const RowRsrc& rs, const RowAux& aux, const uint16_t* chan, int v0,
