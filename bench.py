@@ -444,6 +444,9 @@ def decode_bench(args):
     layers = random_layers(sh, lambda l: gen_weights(wl.config_id, l, sh.d, sh.F), seed=0)
     k_in, k_ff = wl.k_in(), wl.k_ff()
     variants = {"dense": DecodeHarness(sh, layers, args.context + args.steps + args.warmup + 1, ffn="dense")}
+    # the dense FFN on this library's kernels: exact mode keeping every channel
+    variants["dense_library"] = DecodeHarness(sh, layers, args.context + args.steps + args.warmup + 1, ffn="exact",
+                                              k_in=sh.d, k_ff=sh.F)
     for name, ffn in (("prox_int8", "prox"), ("prox_int8_q8rows", "q8")):
         variants[name] = DecodeHarness(sh, layers, args.context + args.steps + args.warmup + 1, ffn=ffn,
                                        proxy="int8", k_in=k_in, k_ff=k_ff)
@@ -492,6 +495,11 @@ def decode_bench(args):
                                   f"batch=1; Prox FFN int8 proxy keep=60% sparsity=70% (k_in={k_in} k_ff={k_ff})"},
            "ms_per_step": {k: round(v, 4) for k, v in ms_graph.items()},
            "speedup_vs_dense": {k: round(ms_graph["dense"] / v, 3) for k, v in ms_graph.items() if k != "dense"},
+           "speedup_vs_dense_library": {k: round(ms_graph["dense_library"] / v, 3) for k, v in ms_graph.items()
+                                        if k.startswith("prox")},
+           "variants": {"dense": "FFN as three bf16 torch products (hipBLASLt)",
+                        "dense_library": "FFN through this library's exact mode with every channel kept (k_ff = d_ff)",
+                        "prox_int8": "Prox FFN, bf16 Stage-2 rows", "prox_int8_q8rows": "Prox FFN, int8 Stage-2 rows"},
            "timing": "ms_per_step: one step captured in a HIP graph and replayed (GPU time; every replay at the "
                      "same cache position); eager_ms_per_step: the same step launched op by op from Python",
            "eager_ms_per_step": {k: round(v, 4) for k, v in ms.items()},

@@ -5,9 +5,12 @@ end-to-end decode step ("Prox: ...", Abstract, reports 1.99x end-to-end at
 the end-to-end gain).
 
 Everything but the FFN is the unchanged decoder block, in torch on the GPU:
-pre-norm RMSNorm (eps 1e-5), q/k/v/o projections (bf16, nn.Linear layout),
-rotary embedding (theta 10000, pairs (2i, 2i + 1)), attention over a bf16 KV
-cache, residuals.  The FFN is one of:
+pre-norm RMSNorm (eps 1e-5), q/k/v/o projections (bf16, nn.Linear layout; q,
+k and v as one product), rotary embedding (theta 10000, pairs (2i, 2i + 1),
+one complex product for q and one for k, the attention scale 1/sqrt(head_dim)
+folded into q's), attention over a bf16 KV cache, residuals, written with few
+kernels so that the step is not dominated by launches of tiny ones.  The FFN
+is one of:
   "dense"  the SwiGLU FFN as three bf16 matrix products (torch / hipBLASLt);
   "prox"   prox_ffn_forward (a proxy kind, k_in, k_ff);
   "q8"     prox_ffn_forward_q8 (int8 Stage-2 rows);
@@ -43,13 +46,6 @@ class DecoderShape:
         return self.d // self.n_heads
 
 
-def _rope_tables(hd: int, max_ctx: int, device):
-    i = torch.arange(hd // 2, dtype=torch.float64)
-    inv = THETA ** (-2.0 * i / hd)
-    ang = torch.arange(max_ctx, dtype=torch.float64)[:, None] * inv[None, :]
-    return torch.cos(ang).float().to(device), torch.sin(ang).float().to(device)
-
-
 class DecodeHarness:
     """Decode steps (batch 1) of a stack of decoder layers with bf16 weights.
 
@@ -64,7 +60,17 @@ class DecodeHarness:
         d, F, hd = shape.d, shape.F, shape.hd
         self.k_in = d if ffn == "exact" else (k_in if k_in is not None else d)
         self.k_ff = k_ff if k_ff is not None else F
-        self.cos, self.sin = _rope_tables(hd, max_ctx, device)
+        # q, k and v projections as one product (rows of wq, wk, wv stacked)
+        self.wqkv = [torch.cat([L["wq"], L["wk"], L["wv"]], 0).contiguous() for L in layers]
+        # rotary factors e^{i pos theta^(-2i/hd)} per position; the query's
+        # carry the attention scale 1/sqrt(hd)
+        i = torch.arange(hd // 2, dtype=torch.float64)
+        ang = torch.arange(max_ctx, dtype=torch.float64)[:, None] * (THETA ** (-2.0 * i / hd))[None, :]
+        rot = torch.polar(torch.ones_like(ang), ang)
+        self.rot_k = rot.to(torch.complex64).to(device)
+        self.rot_q = (rot / math.sqrt(hd)).to(torch.complex64).to(device)
+        self.g_attn = [L["g_attn"].float() for L in layers]
+        self.g_ffn = [L["g_ffn"].float() for L in layers]
         # K cache stored transposed ([kv][hd][ctx]) so q.K is a product with a
         # row-major right operand; V cache [kv][ctx][hd]
         self.Kt = [torch.zeros(shape.n_kv, hd, max_ctx, dtype=torch.bfloat16, device=device) for _ in layers]
@@ -90,15 +96,7 @@ class DecodeHarness:
         self.pos = n
 
     def _rmsnorm(self, x, g):
-        return (x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + EPS) * g.float()).to(torch.bfloat16)
-
-    def _rope(self, v, pos):
-        c, s = self.cos[pos], self.sin[pos]
-        a, b = v[..., 0::2].float(), v[..., 1::2].float()
-        out = torch.empty(v.shape, dtype=torch.float32, device=v.device)
-        out[..., 0::2] = a * c - b * s
-        out[..., 1::2] = a * s + b * c
-        return out.to(torch.bfloat16)
+        return torch.nn.functional.rms_norm(x, (x.shape[-1],), g, EPS).to(torch.bfloat16)
 
     def _ffn(self, li: int, f_in: torch.Tensor) -> torch.Tensor:
         L = self.layers[li]
@@ -115,21 +113,21 @@ class DecodeHarness:
         """x fp32 [1][d] -> fp32 [1][d] after every layer; the cache advances."""
         sh, pos = self.shape, self.pos
         H, KV, hd = sh.n_heads, sh.n_kv, sh.hd
+        d, kvd = sh.d, sh.n_kv * sh.hd
         rep = H // KV
+        T = pos + 1
         for li, L in enumerate(self.layers):
-            a = self._rmsnorm(x, L["g_attn"])
-            q = self._rope(torch.nn.functional.linear(a, L["wq"]).view(H, hd), pos)
-            k = self._rope(torch.nn.functional.linear(a, L["wk"]).view(KV, hd), pos)
-            v = torch.nn.functional.linear(a, L["wv"]).view(KV, hd)
-            self.Kt[li][:, :, pos] = k
-            self.V[li][:, pos, :] = v
-            T = pos + 1
-            qg = q.view(KV, rep, hd)                                   # heads grouped by their kv head
-            sc = torch.matmul(qg, self.Kt[li][:, :, :T]).float() / math.sqrt(hd)
-            p = torch.softmax(sc, dim=-1).to(torch.bfloat16)
-            att = torch.matmul(p, self.V[li][:, :T, :]).reshape(1, sh.d)
-            x = x + torch.nn.functional.linear(att, L["wo"]).float()
-            f_in = self._rmsnorm(x, L["g_ffn"])
+            a = self._rmsnorm(x, self.g_attn[li])
+            qkv = torch.nn.functional.linear(a, self.wqkv[li])                     # [1][d + 2 kvd] bf16
+            qk = torch.view_as_complex(qkv[0, :d + kvd].float().view(H + KV, hd // 2, 2))
+            q = torch.view_as_real(qk[:H] * self.rot_q[pos]).to(torch.bfloat16).view(KV, rep, hd)
+            self.Kt[li][:, :, pos].copy_(torch.view_as_real(qk[H:] * self.rot_k[pos]).view(KV, hd))
+            self.V[li][:, pos, :].copy_(qkv[0, d + kvd:].view(KV, hd))
+            sc = torch.matmul(q, self.Kt[li][:, :, :T])                          # heads grouped by kv head
+            p = torch.softmax(sc, dim=-1, dtype=torch.float32).to(torch.bfloat16)
+            att = torch.matmul(p, self.V[li][:, :T, :]).reshape(1, d)
+            x = x + torch.nn.functional.linear(att, L["wo"])
+            f_in = self._rmsnorm(x, self.g_ffn[li])
             f_out = self._ffn(li, f_in)
             if self.taps is not None:
                 self.taps.setdefault("ffn_in", []).append(f_in.clone())

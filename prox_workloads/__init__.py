@@ -108,6 +108,9 @@ def workloads() -> Dict[str, Workload]:
     s2 = LayerShape(4096, 11008)
     for sp in (50, 70, 90):
         w[f"c2_s{sp}"] = Workload(f"c2_s{sp}", 2, (s2,), 1, "int8", 60, sp, "outlier", 4, 20.0)
+    # every channel kept (sparsity 0): the dense FFN through the same path
+    # (exact mode with k_ff = d_ff is the dense layer on the library's kernels)
+    w["c2_s0"] = Workload("c2_s0", 2, (s2,), 1, "int8", 60, 0, "outlier", 4, 20.0)
     # prefill: the Llama-2-7B layer over 512 tokens at once (every token its
     # own mask; the union of the masks covers nearly every channel)
     w["c2_p512"] = Workload("c2_p512", 2, (s2,), 512, "int8", 60, 70, "outlier", 4, 20.0)
@@ -119,6 +122,7 @@ def workloads() -> Dict[str, Workload]:
         for sp in (50, 70):
             w[f"c4_b{b}_s{sp}"] = Workload(f"c4_b{b}_s{sp}", 4, (s4,), b, "int8", 60, sp,
                                            "outlier", 41, 30.0)
+    w["c4_b1_s0"] = Workload("c4_b1_s0", 4, (s4,), 1, "int8", 60, 0, "outlier", 41, 30.0)
     s5a, s5b = LayerShape(3584, 18944), LayerShape(5120, 13824)
     w["c5"] = Workload("c5", 5, _stack([s5a, s5b], 64), 32, "int4", 60, 80, "rmsnorm")
     return w

@@ -56,7 +56,7 @@ def _run(name, layer=0, tokens=None):
     return c, wl
 
 
-@pytest.mark.parametrize("name", ["c2_s50", "c2_s70", "c2_s90"])
+@pytest.mark.parametrize("name", ["c2_s0", "c2_s50", "c2_s70", "c2_s90"])
 def test_c2_llama7b_layer(name):
     _run(name)
 
