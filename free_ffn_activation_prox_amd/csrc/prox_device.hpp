@@ -275,6 +275,23 @@ __device__ __forceinline__ void load_u32_contig(const uint32_t* __restrict__ src
     for (int q = 0; q < P; ++q) valid[q] = base + q < n;
 }
 
+// Coalesced: 16-byte group g of thread t holds words (g * NT + t) * 4 .. + 3
+// (each wave's load is one contiguous kilobyte).
+template <int P, int NT>
+__device__ __forceinline__ void load_u32_coal(const uint32_t* __restrict__ src, int n, int readable,
+                                              uint32_t (&v)[P], bool (&valid)[P]) {
+    static_assert(P % 4 == 0, "16-byte loads");
+#pragma unroll
+    for (int g = 0; g < P / 4; ++g) {
+        const int i = (g * NT + (int)threadIdx.x) * 4;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (i < readable) u = *reinterpret_cast<const uint4*>(src + i);
+        v[4 * g] = u.x; v[4 * g + 1] = u.y; v[4 * g + 2] = u.z; v[4 * g + 3] = u.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) valid[4 * g + e] = i + e < n;
+    }
+}
+
 template <int P>
 __device__ __forceinline__ void load_u16_contig(const uint16_t* __restrict__ src, int n, int readable,
                                                 uint32_t (&v)[P], bool (&valid)[P]) {

@@ -18,10 +18,14 @@ constexpr int kPartChannels = 128;   // channels per partial-sum slot (the int4 
 constexpr int kGhShift = 17;
 constexpr int kGhBins = 1 << (31 - kGhShift);
 // Stage-2 LDS words holding the histogram (and 64 spare bins for keys past
-// F), then (slow paths) every key of F.
-inline __host__ __device__ int s2_keys_words(int F) {
+// F), then the keys on their way from the coalesced load order to one run of
+// PK per thread (NT runs of PK + 4 words), then (slow paths) every key of F.
+inline __host__ __device__ int s2_keys_words(int F, int NT, int PK) {
     const int kw = (F + 64 + 3) & ~3;
-    return kw > kGhBins + 64 ? kw : kGhBins + 64;
+    const int hw = kGhBins + 64;
+    const int tw = NT * (PK + 4);
+    const int m = kw > hw ? kw : hw;
+    return m > tw ? m : tw;
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -1209,8 +1209,9 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     const int F = a.F, k = a.k, W2 = a.W2;
     const int r0 = split_point(w, F, W2), r1 = split_point(w + 1, F, W2);
     const int L = r1 - r0;                                 // channels of this block's range
-    uint32_t* keys = dyn2;                                 // [s2_keys_words(F)] the key histogram, then every key (index order)
-    uint32_t* cval = keys + s2_keys_words(F);              // [kCandCap + 64] candidate keys, index order
+    uint32_t* keys = dyn2;                                 // [s2_keys_words(F, NT, PK)] the key histogram, then
+                                                           // the keys' transposition, then every key (index order)
+    uint32_t* cval = keys + s2_keys_words(F, NT, PK);      // [kCandCap + 64] candidate keys, index order
     uint16_t* cidx = reinterpret_cast<uint16_t*>(cval + kCandCap + 64);   // [kCandCap + 64] their channels
     uint16_t* kr = cidx + kCandCap + 64;                   // [kCandCap] rank among the kept candidates
     uint16_t* chan = kr + kCandCap;                        // [cap + 64] the block's list
@@ -1235,11 +1236,13 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
     }
     const bool all = k >= F, none = k == 0;
-    // the keys, and the histogram of their high bits cleared meanwhile
+    // the keys in the coalesced order (group g of thread t = keys (g NT + t) 4
+    // .. + 3; the histogram does not depend on which thread holds a key), and
+    // the histogram of their high bits cleared meanwhile
     uint32_t kb[PK];
     {
         bool valid[PK];
-        load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
+        load_u32_coal<PK, NT>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
         if (!all && !none) {
 #pragma unroll
             for (int v = 0; v < kGhBins / NT / 4; ++v)
@@ -1281,6 +1284,29 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 #pragma unroll
             for (int q = 0; q < PK; ++q) valid[q] = (int)kb[q] >= 0;
             st = block_coarse_bin<PK, NT>(kb, valid, k, 31, hist, sc);
+        }
+    }
+    // ---- the keys to one run per thread: thread t takes keys t PK .. t PK +
+    // PK - 1 (the index-order ranks below come from one block scan of the
+    // runs).  Through LDS (the histogram is no longer read): run t at word
+    // t (PK + 4), so the 16-byte reads of the 64 lanes fall in distinct banks.
+    {
+#pragma unroll
+        for (int g = 0; g < PK / 4; ++g) {
+            const int j = (g * NT + t) * 4;                 // the 4 keys share one run (PK % 4 == 0)
+            *reinterpret_cast<uint4*>(keys + j + 4 * (j / PK)) = make_uint4(kb[4 * g], kb[4 * g + 1],
+                                                                            kb[4 * g + 2], kb[4 * g + 3]);
+        }
+        lds_barrier();
+        const uint32_t sink = 0x80000000u | ((uint32_t)(t & 63) << kGhShift);
+#pragma unroll
+        for (int g = 0; g < PK / 4; ++g) {
+            const uint4 u = *reinterpret_cast<const uint4*>(keys + t * (PK + 4) + 4 * g);
+            const int j = t * PK + 4 * g;
+            kb[4 * g] = j < F ? u.x : sink;
+            kb[4 * g + 1] = j + 1 < F ? u.y : sink;
+            kb[4 * g + 2] = j + 2 < F ? u.z : sink;
+            kb[4 * g + 3] = j + 3 < F ? u.w : sink;
         }
     }
     // bin of a key = (int)key >> shift: certain above cert_gt, candidate at
@@ -1597,7 +1623,7 @@ template <int PK, int R, int G, int MODE>
 static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
     // list length bound: ceil(C/W2) + ceil(KC/W2); selection only keeps no list
     const int cap = MODE != 0 ? (a.k + a.W2 - 1) / a.W2 + 2 : 0;
-    const size_t dyn = (size_t)s2_keys_words(a.F) * 4 + ((size_t)kCandCap + 64) * 4 +
+    const size_t dyn = (size_t)s2_keys_words(a.F, kS2Threads, PK) * 4 + ((size_t)kCandCap + 64) * 4 +
                        ((size_t)kCandCap * 2 + 64 + cap + 64) * 2;
     auto fn = k_stage2<PK, R, G, MODE>;
     if (dyn > 48 * 1024) {
