@@ -56,7 +56,7 @@ class _QWeights(ctypes.Structure):
 class _Taps(ctypes.Structure):
     _fields_ = [("in_idx", ctypes.c_void_p), ("key", ctypes.c_void_p), ("h_hat", ctypes.c_void_p),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("stream_idx", ctypes.c_void_p), ("timeline", ctypes.c_void_p)]
+                ("event_mode", ctypes.c_int32), ("stream_idx", ctypes.c_void_p), ("timeline", ctypes.c_void_p)]
 
 
 N_PHASES = 3
@@ -253,12 +253,15 @@ def alloc_workspace(d_model: int, d_ff: int, batch: int, kind: str, device="cuda
 
 
 def ffn_forward(x, weights, proxy: Proxy, k_in: int, k_ff: int, *, y=None, mask=None,
-                idx=None, workspace=None, taps: bool = False, events=None, stream=None):
+                idx=None, workspace=None, taps: bool = False, events=None, kernel_events: bool = False,
+                stream=None):
     """Sparse SwiGLU forward for x [B][d] bf16.  Returns (y fp32 [B][d], mask u8 [B][F],
     idx int32 [B][k_ff]) and, with ``taps``, a dict of in_idx / key / h_hat.
-    ``events``: N_PHASES + 1 events recorded at the phase boundaries on the
-    launch stream (measurement hook): torch.cuda.Event(enable_timing=True)
-    objects already recorded once, or raw hipEvent_t handles (int)."""
+    ``events`` (measurement hook): torch.cuda.Event(enable_timing=True) objects
+    already recorded once, or raw hipEvent_t handles (int).  By default
+    N_PHASES + 1 events recorded at the phase boundaries on the launch stream;
+    with ``kernel_events``, 2 * N_PHASES events carried by the kernels
+    themselves: events[2p] .. events[2p + 1] spans phase p's kernels alone."""
     import torch
     if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
         raise ValueError("x must be a contiguous 2-D bf16 CUDA tensor")
@@ -277,7 +280,7 @@ def ffn_forward(x, weights, proxy: Proxy, k_in: int, k_ff: int, *, y=None, mask=
     sp = _stream_ptr(stream)
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*[getattr(e, "cuda_event", e) for e in events])
-        ct = _Taps(None, None, None, arr, len(events), 0, None, None)
+        ct = _Taps(None, None, None, arr, len(events), 1 if kernel_events else 0, None, None)
         _call_forward(q8, x, B, weights, proxy, k_in, k_ff, y, mask, idx, workspace, ct, sp)
         return y, mask, idx[:, :k_ff]
     if taps:

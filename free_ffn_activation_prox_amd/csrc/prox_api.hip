@@ -196,7 +196,8 @@ prox_status forward_impl(const void* x, int32_t batch, int d, int F, const S2Row
         // follow the sub-batch, the phase events time the last one
         const WsLayout Lc = ws_layout(d, F, PROX_CHUNK_BATCH, p->kind);
         if (ws_bytes < Lc.total) return fail(PROX_E_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, Lc.total);
-        void* const* ev = (taps && taps->events && taps->n_events >= PROX_N_PHASES + 1) ? taps->events : nullptr;
+        void* const* ev = (taps && taps->events && taps->event_mode == 0 && taps->n_events >= PROX_N_PHASES + 1)
+                              ? taps->events : nullptr;
         if (ev) {
             hipError_t e = hipEventRecord((hipEvent_t)ev[0], (hipStream_t)stream);
             if (e != hipSuccess) return hip_fail(e, "event record");
@@ -213,6 +214,7 @@ prox_status forward_impl(const void* x, int32_t batch, int d, int F, const S2Row
                 t.stream_idx = taps->stream_idx ? taps->stream_idx + (size_t)c0 * k_ff : nullptr;
                 t.events = last ? taps->events : nullptr;
                 t.n_events = last ? taps->n_events : 0;
+                t.event_mode = taps->event_mode;
                 tp = &t;
             }
             const prox_status st = forward_impl(static_cast<const uint16_t*>(x) + (size_t)c0 * d, nb, d, F, rows, p,
@@ -240,8 +242,23 @@ prox_status forward_impl(const void* x, int32_t batch, int d, int F, const S2Row
     // 256, whose longer rows keep more bytes in flight per block)
     const int W2 = stage2_blocks(batch, k_ff, batch >= kBatchMin || d <= 4096 ? n_cu : n_cu * 3 / 4);
 
-    void* const* ev = (taps && taps->events && taps->n_events >= PROX_N_PHASES + 1) ? taps->events : nullptr;
+    // measurement events: mode 0 records events[i] on the stream at phase
+    // boundary i; mode 1 hands phase i's pair (events[2i], events[2i + 1]) to
+    // its kernels' launches (the guard clears them on every return)
+    const int emode = taps ? taps->event_mode : 0;
+    void* const* ev = (taps && taps->events && emode == 0 && taps->n_events >= PROX_N_PHASES + 1) ? taps->events
+                                                                                                  : nullptr;
+    void* const* kev = (taps && taps->events && emode == 1 && taps->n_events >= 2 * PROX_N_PHASES) ? taps->events
+                                                                                                   : nullptr;
+    struct EventsGuard {
+        ~EventsGuard() { launch_events() = LaunchEvents{}; }
+    } events_guard;
     auto mark = [&](int i) -> hipError_t {
+        if (kev) {
+            launch_events() = i < PROX_N_PHASES ? LaunchEvents{(hipEvent_t)kev[2 * i], (hipEvent_t)kev[2 * i + 1]}
+                                                : LaunchEvents{};
+            return hipSuccess;
+        }
         return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess;
     };
 

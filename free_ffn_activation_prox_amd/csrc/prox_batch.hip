@@ -143,9 +143,9 @@ __global__ void __launch_bounds__(NT) k_xsel(const uint16_t* __restrict__ x, int
 hipError_t launch_xsel(const uint16_t* x, int B, int d, int k_in, uint16_t* xm, int32_t* in_idx,
                        hipStream_t s) {
     const int per_block = (d + kXselPer - 1) / kXselPer;
-    if (per_block <= 256) hipLaunchKernelGGL(k_xsel<256>, dim3(B), dim3(256), 0, s, x, d, k_in, xm, in_idx);
-    else if (per_block <= 512) hipLaunchKernelGGL(k_xsel<512>, dim3(B), dim3(512), 0, s, x, d, k_in, xm, in_idx);
-    else hipLaunchKernelGGL(k_xsel<1024>, dim3(B), dim3(1024), 0, s, x, d, k_in, xm, in_idx);
+    if (per_block <= 256) launch_kernel(k_xsel<256>, dim3(B), dim3(256), 0, s, x, d, k_in, xm, in_idx);
+    else if (per_block <= 512) launch_kernel(k_xsel<512>, dim3(B), dim3(512), 0, s, x, d, k_in, xm, in_idx);
+    else launch_kernel(k_xsel<1024>, dim3(B), dim3(1024), 0, s, x, d, k_in, xm, in_idx);
     return hipGetLastError();
 }
 
@@ -432,7 +432,7 @@ static hipError_t go_proxy_batch(const PbArgs& a, hipStream_t s) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(a.tiles * a.ks1), dim3(NW * 64), dyn, s, a);
+    launch_kernel(fn, dim3(a.tiles * a.ks1), dim3(NW * 64), dyn, s, a);
     return hipGetLastError();
 }
 
@@ -780,10 +780,10 @@ template <int NG>
 static hipError_t go_gateup_down(const GuArgs& gu, const DnArgs& dn, hipStream_t s) {
     // two M-tiles per wave when x has two or more token groups (x operand reuse)
     constexpr int MTW = NG >= 2 ? 2 : 1;
-    hipLaunchKernelGGL((k_gateup_batch<NG, MTW>), dim3((gu.F + 16 * MTW - 1) / (16 * MTW)), dim3(256), 0, s, gu);
+    launch_kernel(k_gateup_batch<NG, MTW>, dim3((gu.F + 16 * MTW - 1) / (16 * MTW)), dim3(256), 0, s, gu);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_down_batch<NG>, dim3((dn.d + kDnCols - 1) / kDnCols, dn.KS), dim3(256), 0, s, dn);
+    launch_kernel(k_down_batch<NG>, dim3((dn.d + kDnCols - 1) / kDnCols, dn.KS), dim3(256), 0, s, dn);
     return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ hipError_t launch_exact_h(const uint16_t* x, int B, int d, const uint16_t* wg_t,
         hipError_t e = hipFuncSetAttribute((const void*)k_exact_h, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_exact_h, dim3(nb, B), dim3(kExThreads), dyn, s, x, wg_t, wu_t, d, F, f_pad, key, hbuf,
+    launch_kernel(k_exact_h, dim3(nb, B), dim3(kExThreads), dyn, s, x, wg_t, wu_t, d, F, f_pad, key, hbuf,
                        h_tap, key_tap, in_idx_tap, tl);
     return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // Host-side declarations shared by the Prox library's translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -127,6 +128,29 @@ inline WsLayout ws_layout(int d, int F, int B, int kind) {
     L.hx = o;     o = align_up(o + (kind == 3 ? (size_t)B * F * 8 : 0), 256);
     L.total = o;
     return L;
+}
+
+// Kernel-carried measurement events (event mode 1 of the taps), per host
+// thread: while set, the next forward launch takes `start` at its start (and
+// clears it) and every launch takes `stop` at its end, so after a phase the
+// pair spans its first kernel's start to its last kernel's end.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchEvents& launch_events() {
+    static thread_local LaunchEvents e;
+    return e;
+}
+// Every kernel of a forward is launched through here.
+template <typename K, typename... Args>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args) {
+    LaunchEvents& e = launch_events();
+    if (e.start || e.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, e.start, e.stop, 0u, args...);
+        e.start = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+    }
 }
 
 // ---- launchers (prox_kernels.hip); all enqueue on `s` and return the launch status

@@ -934,7 +934,7 @@ static hipError_t go_stage1(const Stage1Args& a, int B, hipStream_t s) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(a.nb1, B), dim3(kS1Threads), dyn, s, a);
+    launch_kernel(fn, dim3(a.nb1, B), dim3(kS1Threads), dyn, s, a);
     return hipGetLastError();
 }
 
@@ -1630,7 +1630,7 @@ static hipError_t go_stage2(const Stage2Args& a, int B, hipStream_t s) {
         hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3(a.W2, B), dim3(kS2Threads), dyn, s, a);
+    launch_kernel(fn, dim3(a.W2, B), dim3(kS2Threads), dyn, s, a);
     return hipGetLastError();
 }
 
@@ -1732,7 +1732,7 @@ __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypar
 }
 
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s) {
-    hipLaunchKernelGGL(k_reduce_y, dim3((d + kRedCols - 1) / kRedCols, B), dim3(256), 0, s, ypart, d,
+    launch_kernel(k_reduce_y, dim3((d + kRedCols - 1) / kRedCols, B), dim3(256), 0, s, ypart, d,
                        W2, y);
     return hipGetLastError();
 }

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PROX_ABI_VERSION 3
+#define PROX_ABI_VERSION 4
 
 typedef enum {
     PROX_OK = 0,
@@ -120,14 +120,21 @@ typedef struct {
  *   in_idx [batch][k_in]   kept inputs of Stage 1, ascending
  *   key    [batch][d_ff]   fp32 ranking key |h~_j|
  *   h_hat  [batch][d_ff]   fp64 approximate intermediate h~_j (signed)
- * Measurement hook (host, nullable): `events` holds n_events >= PROX_N_PHASES + 1
- * hipEvent_t handles (as void*) created by the caller; events[0] is recorded on
- * the stream before the first launch and events[p + 1] after phase p.  A phase
- * is one kernel below 4 tokens per call; from 4 tokens stage 1 is the input
- * selection and the proxy GEMM, stage 2 the channel selection, gate/up and
- * down projections.  Above PROX_CHUNK_BATCH tokens the events time the last
- * sub-batch (events[0] is still recorded before the first).  The other taps
- * cover every token.
+ * Measurement hook (host, nullable): `events` holds hipEvent_t handles (as
+ * void*) created by the caller, used in one of two ways (`event_mode`):
+ *   0  n_events >= PROX_N_PHASES + 1: events[0] is recorded on the stream
+ *      before the first launch and events[p + 1] after phase p (the interval
+ *      also holds the dispatch of the phase's first kernel);
+ *   1  n_events >= 2 * PROX_N_PHASES: the kernels themselves carry the events
+ *      (hipExtLaunchKernel): events[2p] takes the start of phase p's first
+ *      kernel and events[2p + 1] the end of its last one, so one kernel's
+ *      interval is its execution alone.  A phase with no kernel leaves its
+ *      pair unrecorded.
+ * A phase is one kernel below 4 tokens per call; from 4 tokens stage 1 is the
+ * input selection and the proxy GEMM, stage 2 the channel selection, gate/up
+ * and down projections.  Above PROX_CHUNK_BATCH tokens the events time the
+ * last sub-batch (mode 0: events[0] is still recorded before the first).  The
+ * other taps cover every token.
  *   stream_idx [batch][k_ff]  below 4 tokens per call only (untouched from 4):
  *          the channels whose rows the Stage-2 blocks actually stream, each
  *          block's list at the ranks of its share; over all blocks a
@@ -136,14 +143,16 @@ typedef struct {
  *          real-time counter, stored by each block of Stage 1 (index 0) and
  *          Stage 2 (index 1; block = token * blocks per token + block) at
  *          points 0 start, 1 selection done, 2 stream done (Stage 1: of its
- *          last tile), 3 end; points 4-7 unused.                              */
+ *          last tile), 3 end, and inside the selections: Stage 1 4 histogram
+ *          built, 5 threshold found, 6 first scan done; Stage 2 4 histogram
+ *          built, 5 keys classified, 6 lists written, 7 candidates ranked.  */
 typedef struct {
     int32_t* in_idx;
     float* key;
     double* h_hat;
     void* const* events;
     int32_t n_events;
-    int32_t reserved;
+    int32_t event_mode;
     int32_t* stream_idx;
     uint64_t* timeline;
 } prox_taps;

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.abi_version() == 3
+    assert P.abi_version() == 4
 
 
 def _align(v, a):

@@ -194,6 +194,33 @@ def test_measurement_events(B):
     assert all(0.0 < t < 1000.0 for t in times), times
 
 
+@pytest.mark.parametrize("B", [1, 8])
+def test_kernel_events(B):
+    # event mode 1: each phase's kernels carry a start/stop pair; outputs are
+    # unchanged, every phase interval is positive and the phases, run back to
+    # back, fit inside the boundary events of the same call (mode 0)
+    import free_ffn_activation_prox_amd as P
+    c = _case(1024, 1500, B, seed=13, kind="int8")
+    ref = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 450)
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * P.N_PHASES)]
+    for e in kev:
+        e.record()
+    torch.cuda.synchronize()
+    out = P.ffn_forward(c.dx, c.weights, c.proxy, 600, 450, events=kev, kernel_events=True)
+    torch.cuda.synchronize()
+    for u, v in zip(out, ref):
+        assert torch.equal(u, v)
+    ktimes = [kev[2 * p].elapsed_time(kev[2 * p + 1]) for p in range(P.N_PHASES)]
+    assert all(0.0 < t < 1000.0 for t in ktimes), ktimes
+    # phase p ends before phase p + 1 starts (stream order)
+    for p in range(P.N_PHASES - 1):
+        assert kev[2 * p + 1].elapsed_time(kev[2 * p + 2]) >= 0.0
+    # a later plain call is not timed by the pairs (the library forgets them)
+    P.ffn_forward(c.dx, c.weights, c.proxy, 600, 450)
+    torch.cuda.synchronize()
+    assert [kev[2 * p].elapsed_time(kev[2 * p + 1]) for p in range(P.N_PHASES)] == ktimes
+
+
 @pytest.mark.parametrize("B,kind", [(1, "int4"), (2, "int8"), (8, "int4"), (8, "int8")])
 def test_graph_replay(B, kind):
     # one forward captured in a HIP graph and replayed several times with new
