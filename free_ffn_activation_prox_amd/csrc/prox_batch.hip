@@ -60,34 +60,19 @@ __device__ __forceinline__ uint32_t pair_bf16(int qa, int qb) {
 
 // ===========================================================================
 // Input selection: one block per token.  Thread t holds x[16t .. 16t + 15].
-// Keys are |x| as bf16 bits (sign cleared), so the order of keys is the order
-// of magnitudes.  T = the k-th largest key is found bit by bit from the top
-// (the largest value with at least k keys >= it), each bit one block count;
-// keys above T are kept and keys equal to T are kept in index order until k
-// are kept.
+// Keys are |x| as bf16 bits (sign cleared, 15 bits), so the order of keys is
+// the order of magnitudes.  T = the k-th largest key: a 2048-bin LDS
+// histogram of key >> 4 gives its bin (one block scan), a 16-bin histogram of
+// the low 4 bits of the keys in that bin gives T itself; keys above T are kept
+// and keys equal to T are kept in index order until k are kept.
 // ===========================================================================
 constexpr int kXselPer = 16;   // keys per thread; blocks of d / 16 threads (d <= 16384)
-
-// Number of (valid) keys >= v over the block; `slot` = NT / 64 ints of LDS
-// not in use by the previous call (callers alternate two slot sets).
-template <int NT>
-__device__ __forceinline__ int xsel_count_ge(const uint32_t (&key)[kXselPer], const bool (&valid)[kXselPer],
-                                             uint32_t v, int* slot) {
-    int c = 0;
-#pragma unroll
-    for (int q = 0; q < kXselPer; ++q) c += __popcll(__ballot(valid[q] && key[q] >= v));
-    if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = c;
-    lds_barrier();
-    int tot = 0;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) tot += slot[i];
-    return tot;
-}
 
 template <int NT>
 __global__ void __launch_bounds__(NT) k_xsel(const uint16_t* __restrict__ x, int d, int k,
                                                       uint16_t* __restrict__ xm, int32_t* __restrict__ in_idx) {
     __shared__ int sc[2][32];
+    __shared__ uint32_t hist[2048 + 16];
     const int b = blockIdx.x, t = threadIdx.x;
     uint32_t v[kXselPer], key[kXselPer];
     bool valid[kXselPer];
@@ -99,12 +84,33 @@ __global__ void __launch_bounds__(NT) k_xsel(const uint16_t* __restrict__ x, int
     uint32_t T = 0;
     int cgt = 0;
     if (!all && !none) {
-        int round = 0;
-        for (int bit = 14; bit >= 0; --bit, ++round) {
-            const uint32_t cand = T | (1u << bit);
-            if (xsel_count_ge<NT>(key, valid, cand, sc[round & 1]) >= k) T = cand;
+        for (int i = t; i < 2048 + 16; i += NT) hist[i] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < kXselPer; ++q)
+            if (valid[q]) atomicAdd(&hist[key[q] >> 4], 1u);
+        lds_barrier();
+        uint32_t tb;
+        int above;
+        find_bin<NT>(hist, 2048, k, sc[0], tb, above);   // T's bin; `above` keys in higher bins
+#pragma unroll
+        for (int q = 0; q < kXselPer; ++q)
+            if (valid[q] && (key[q] >> 4) == tb) atomicAdd(&hist[2048 + (key[q] & 15u)], 1u);
+        lds_barrier();
+        // every thread walks the 16 low-bit bins from the top
+        int cum = above;
+        bool found = false;
+        T = tb << 4;
+#pragma unroll
+        for (int v2 = 15; v2 >= 0; --v2) {
+            const int c = (int)hist[2048 + v2];
+            if (!found && cum + c >= k) {
+                T = (tb << 4) + (uint32_t)v2;
+                found = true;
+            }
+            cum += found ? 0 : c;
         }
-        cgt = xsel_count_ge<NT>(key, valid, T + 1u, sc[round & 1]);   // round 15: the other slot set
+        cgt = cum;                                         // keys > T
     }
     const int need = k - cgt;   // keys equal to T that are kept, lowest indices first
     int neq = 0;

@@ -1192,6 +1192,11 @@ constexpr int kCandCap = 1024;    // candidates listed in LDS (more: the slow pa
 
 template <int PK, int R, int G, int MODE>
 __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
+    // Keys per thread from 32 up are loaded coalesced and transposed through
+    // LDS; fewer are loaded as each thread's own run directly (its 16-byte
+    // loads span at most 96 bytes per lane, and the transposition would cost
+    // more than it saves).
+    constexpr bool kS2CoalescedKeys = PK >= 32;
     constexpr bool STREAM = MODE != 0;       // 0: selection only (mask and idx)
     constexpr int SM = STREAM ? MODE : 1;    // the stream code's mode (unused when MODE == 0)
     constexpr int NT = kS2Threads;
@@ -1236,13 +1241,17 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
         for (int e = 0; e < 8; ++e) yacc[r][e] = 0.f;
     }
     const bool all = k >= F, none = k == 0;
-    // the keys in the coalesced order (group g of thread t = keys (g NT + t) 4
-    // .. + 3; the histogram does not depend on which thread holds a key), and
-    // the histogram of their high bits cleared meanwhile
+    // the keys (from 32 per thread in the coalesced order, group g of thread t
+    // = keys (g NT + t) 4 .. + 3: the histogram does not depend on which
+    // thread holds a key; else thread t's own run), and the histogram of their
+    // high bits cleared meanwhile
     uint32_t kb[PK];
     {
         bool valid[PK];
-        load_u32_coal<PK, NT>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
+        if constexpr (kS2CoalescedKeys)
+            load_u32_coal<PK, NT>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
+        else
+            load_u32_contig<PK>(reinterpret_cast<const uint32_t*>(keyb), F, a.f_pad, kb, valid);
         if (!all && !none) {
 #pragma unroll
             for (int v = 0; v < kGhBins / NT / 4; ++v)
@@ -1286,11 +1295,11 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             st = block_coarse_bin<PK, NT>(kb, valid, k, 31, hist, sc);
         }
     }
-    // ---- the keys to one run per thread: thread t takes keys t PK .. t PK +
-    // PK - 1 (the index-order ranks below come from one block scan of the
-    // runs).  Through LDS (the histogram is no longer read): run t at word
+    // ---- coalesced keys to one run per thread: thread t takes keys t PK ..
+    // t PK + PK - 1 (the index-order ranks below come from one block scan of
+    // the runs).  Through LDS (the histogram is no longer read): run t at word
     // t (PK + 4), so the 16-byte reads of the 64 lanes fall in distinct banks.
-    {
+    if constexpr (kS2CoalescedKeys) {
 #pragma unroll
         for (int g = 0; g < PK / 4; ++g) {
             const int j = (g * NT + t) * 4;                 // the 4 keys share one run (PK % 4 == 0)
