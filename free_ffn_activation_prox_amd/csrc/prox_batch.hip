@@ -370,26 +370,35 @@ __global__ void __launch_bounds__(KIND == 1 ? 256 : 512) k_proxy_batch(PbArgs a)
         if (t == 0) flag = tile_arrive(a.tcnt + tile, a.gen, a.ks1);
         __syncthreads();
         if (!flag) return;
+        // the splits in order; each split's 2 NG loads are in flight together
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int n = 16 * g + r;
-                if (n < a.B) {
-                    double sum[4] = {0.0, 0.0, 0.0, 0.0};
-                    for (int sp = 0; sp < a.ks1; ++sp) {
-                        const uint32_t off =
-                            ((((uint32_t)sp * 2u + m) * (uint32_t)a.B + n) * (uint32_t)a.f_pad + ch0 + 4 * q4) * 4u;
-                        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rp, (int)off, 0, kCoherent);
-                        sum[0] += (double)__uint_as_float(v.x);
-                        sum[1] += (double)__uint_as_float(v.y);
-                        sum[2] += (double)__uint_as_float(v.z);
-                        sum[3] += (double)__uint_as_float(v.w);
-                    }
+            for (int g = 0; g < NG; ++g)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dacc[m][g][i] = sum[i];
+                for (int i = 0; i < 4; ++i) dacc[m][g][i] = 0.0;
+        for (int sp = 0; sp < a.ks1; ++sp) {
+            u32x4_t v[2][NG];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int n = 16 * g + r;
+                    const uint32_t off =
+                        ((((uint32_t)sp * 2u + m) * (uint32_t)a.B + n) * (uint32_t)a.f_pad + ch0 + 4 * q4) * 4u;
+                    v[m][g] = n < a.B ? __builtin_amdgcn_raw_buffer_load_b128(rp, (int)off, 0, kCoherent)
+                                      : u32x4_t{0u, 0u, 0u, 0u};
                 }
-            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    dacc[m][g][0] += (double)__uint_as_float(v[m][g].x);
+                    dacc[m][g][1] += (double)__uint_as_float(v[m][g].y);
+                    dacc[m][g][2] += (double)__uint_as_float(v[m][g].z);
+                    dacc[m][g][3] += (double)__uint_as_float(v[m][g].w);
+                }
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -491,21 +500,34 @@ __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
     constexpr int PD = MTW == 1 ? 4 : 3;   // stages in flight
     constexpr int CH = 16 * MTW;           // channels of the block
     __shared__ uint32_t used[CH];
+    __shared__ uint8_t mk[16 * NG][CH];     // the tokens' mask bytes of the block's channels
     __shared__ float red[4][NG][2][4][64];
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int r = l & 15, q4 = l >> 4;
     const int j0 = blockIdx.x * CH;
     const int d = a.d;
 
-    // channels of this block that some token keeps
-    if (t < CH) used[t] = 0u;
+    // the mask bytes of the block's channels (every load issued before the
+    // first is waited for), then the channels that some token keeps
+    {
+        constexpr int NE = (16 * NG * CH + 255) / 256;
+        uint8_t mv[NE];
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = t + 256 * u, n = e / CH, c = e % CH;
+            mv[u] = (n < a.B && j0 + c < a.F) ? a.mask[(size_t)n * a.F + j0 + c] : (uint8_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < NE; ++u) {
+            const int e = t + 256 * u;
+            if (e < 16 * NG * CH) mk[e / CH][e % CH] = mv[u];
+        }
+    }
     __syncthreads();
-    for (int c = t % CH, n0 = t / CH; c < CH && n0 < 256 / CH; c += 256) {
-        const int jr = j0 + c;
+    if (t < CH) {
         uint32_t any = 0;
-        if (jr < a.F)
-            for (int n = n0; n < a.B; n += 256 / CH) any |= a.mask[(size_t)n * a.F + jr];
-        if (any) used[c] = 1u;
+        for (int n = 0; n < a.B; ++n) any |= mk[n][t];
+        used[t] = any ? 1u : 0u;
     }
     __syncthreads();
 
@@ -610,7 +632,7 @@ __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
                         uu += red[v][g][1][i][l];
                     }
                     float hv = gg / (1.f + expf(-gg)) * uu;
-                    if (jc >= a.F || !a.mask[(size_t)n * a.F + jc]) hv = 0.f;
+                    if (jc >= a.F || !mk[n][16 * mt + 4 * q4 + i]) hv = 0.f;
                     const uint32_t hi = bf16_rne(hv);
                     const uint32_t lo = bf16_rne(hv - __uint_as_float(hi << 16));
                     a.hb[(size_t)n * a.f_pad + jc] = (uint16_t)hi;
