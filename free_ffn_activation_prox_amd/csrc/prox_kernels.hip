@@ -1207,7 +1207,6 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     __shared__ int sc[24];
     __shared__ int wc[4][NW];
     __shared__ float red[2][NW * 2 * G];
-    __shared__ uint16_t chan_sink[kWave];                // stores of keys that list nothing
 
     tl_mark(a.tl, 1, 0);
     const int w = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
@@ -1317,6 +1316,13 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             kb[4 * g + 2] = j + 2 < F ? u.z : sink;
             kb[4 * g + 3] = j + 3 < F ? u.w : sink;
         }
+    } else {
+        // the thread's own run at the same place, for the candidate listing
+        // below (each thread reads back only what it wrote: no barrier)
+#pragma unroll
+        for (int g = 0; g < PK / 4; ++g)
+            *reinterpret_cast<uint4*>(keys + t * (PK + 4) + 4 * g) =
+                make_uint4(kb[4 * g], kb[4 * g + 1], kb[4 * g + 2], kb[4 * g + 3]);
     }
     // bin of a key = (int)key >> shift: certain above cert_gt, candidate at
     // cand_eq (keep-all: every valid key certain; keep-none: nothing)
@@ -1350,29 +1356,22 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
     int nc = listed ? c1 - c0 : 0;
     if (listed) {
         // share: the certain keys of rank [c0, c1) into chan; candidates
-        // (index order) into cidx / cval.  Every key of the thread takes one
-        // store, to its slot or to a per-lane sink past the arrays' ends, so
-        // the loops have no branches.
-        const int lane = t & (kWave - 1);
+        // (index order) into cidx / cval.  The loops visit only the set bits
+        // of the thread's masks (the lowest first, so in index order); a
+        // candidate's key is read back from the thread's run in LDS (after
+        // keys_to_lds the run sits at t PK, else at t (PK + 4)).
         if (STREAM && crank0 < c1 && crank0 + ncert_t > c0) {
             int cr = crank0;
-#pragma unroll
-            for (int q = 0; q < PK; ++q) {
-                const bool c = (cem >> q) & 1ull;
-                const bool on = c && cr >= c0 && cr < c1;
-                *(on ? chan + (cr - c0) : chan_sink + lane) = (uint16_t)(t * PK + q);
-                cr += c ? 1 : 0;
-            }
+            for (uint64_t m = cem; m != 0ull && cr < c1; m &= m - 1ull, ++cr)
+                if (cr >= c0) chan[cr - c0] = (uint16_t)(t * PK + __builtin_ctzll(m));
         }
         if (nd > 0) {
+            const uint32_t* run = keys + (ncand > kSmallCand ? t * PK : t * (PK + 4));
             int cp = cp0;
-#pragma unroll
-            for (int q = 0; q < PK; ++q) {
-                const bool on = (cdm >> q) & 1ull;
-                const int i = on ? cp : kCandCap + lane;
-                cidx[i] = (uint16_t)(t * PK + q);
-                cval[i] = kb[q];
-                cp += on ? 1 : 0;
+            for (uint64_t m = cdm; m != 0ull; m &= m - 1ull, ++cp) {
+                const int q = __builtin_ctzll(m);
+                cidx[cp] = (uint16_t)(t * PK + q);
+                cval[cp] = run[q];
             }
         }
     }
