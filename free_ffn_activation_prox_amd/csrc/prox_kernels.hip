@@ -1534,13 +1534,16 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
 
     // ---- the range: kept flags, idx and mask (after the stream: nothing in
     // the stream depends on them)
+    // (keys past the first NT of the range come from LDS: the threads' runs
+    // at t (PK + 4), or every key in index order after keys_to_lds)
     auto write_range = [&]() {
     if (listed && (a.idx || a.mask)) {
+        const bool idx_order = ncand > kSmallCand;
         int nk = 0, nd_run = 0;
         for (int c0r = 0; c0r < L; c0r += NT) {
             const int j = r0 + c0r + t;
             const bool in = c0r + t < L;
-            const uint32_t v = c0r == 0 ? own0 : (in ? __float_as_uint(keyb[j]) : 0u);
+            const uint32_t v = c0r == 0 ? own0 : (in ? keys[idx_order ? j : (j / PK) * (PK + 4) + j % PK] : 0u);
             bool p1[1] = {in && is_cand(v)};
             int pos1[1], t1[1];
             block_ballot_pos<kS2Threads, 1>(p1, wc, pos1, t1);
