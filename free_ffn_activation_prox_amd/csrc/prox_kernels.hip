@@ -1398,9 +1398,17 @@ __global__ void __launch_bounds__(kS2Threads) k_stage2(Stage2Args a) {
             const bool has = t < ncand;
             const uint32_t v = has ? cval[t] : 0u;
             int rank = 0;
-            for (int i = 0; i < ncand; ++i) {
-                const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, i);
-                rank += (u > v || (u == v && i < t)) ? 1 : 0;
+            // eight lanes' keys per pass, so the reads are not one long
+            // dependent chain
+            for (int i0 = 0; i0 < ncand; i0 += 8) {
+                uint32_t u[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = (uint32_t)__builtin_amdgcn_readlane((int)v, (i0 + e) & 63);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = i0 + e;
+                    rank += (i < ncand && (u[e] > v || (u[e] == v && i < t))) ? 1 : 0;
+                }
             }
             const bool kept = has && rank < st.krem;
             const uint64_t km = __ballot(kept);
