@@ -868,20 +868,33 @@ __global__ void __launch_bounds__(kS1Threads) k_stage1(Stage1Args a) {
         }
         tl_mark(a.tl, 0, 2);
         // reduce the 8 row slots of the wave (lanes l ^ 8, l ^ 16, l ^ 32 share the
-        // channel block), then the 8 waves, in a fixed order
+        // channel block), then the 8 waves, in a fixed order.  The slots are
+        // added pairwise over lane bits 3, 4 and 5 with each level halving
+        // what a lane keeps (bit 3 picks the matrix, bits 4 and 5 the channel
+        // halves), so every lane ends with 2 of the wave's 128 sums; the
+        // pairing, hence every rounding, is that of a full reduction over
+        // the three lane bits.
+        {
+            const bool b3 = (l & 8) != 0, b4 = (l & 16) != 0, b5 = (l & 32) != 0;
+            double w8[8], w4[4], w2[2];
 #pragma unroll
-        for (int c = 0; c < NV; ++c) {
-            ag[c] += dpp_ror8(ag[c]);
-            au[c] += dpp_ror8(au[c]);
-            ag[c] = xor32_add(xor16_add(ag[c]));
-            au[c] = xor32_add(xor16_add(au[c]));
-        }
-        if (l < 8) {
-#pragma unroll
-            for (int c = 0; c < NV; ++c) {
-                red[w][0][cb * NV + c] = ag[c];
-                red[w][1][cb * NV + c] = au[c];
+            for (int c = 0; c < 8; ++c) {
+                const double send = b3 ? ag[c] : au[c];
+                w8[c] = (b3 ? au[c] : ag[c]) + dpp_ror8(send);
             }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const double send = b4 ? w8[c] : w8[c + 4];
+                w4[c] = (b4 ? w8[c + 4] : w8[c]) + __shfl_xor(send, 16, kWave);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const double send = b5 ? w4[c] : w4[c + 2];
+                w2[c] = (b5 ? w4[c + 2] : w4[c]) + __shfl_xor(send, 32, kWave);
+            }
+            const int ch = cb * NV + (b4 ? 4 : 0) + (b5 ? 2 : 0);
+            red[w][b3 ? 1 : 0][ch] = w2[0];
+            red[w][b3 ? 1 : 0][ch + 1] = w2[1];
         }
         lds_barrier();
         if (t < 2 * TC) {
