@@ -340,6 +340,10 @@ __global__ void __launch_bounds__(KIND == 1 ? 256 : 512) k_proxy_batch(PbArgs a)
             __builtin_amdgcn_sched_barrier(0);
             load_stage(s0 + i + PD, ring[i]);
             __builtin_amdgcn_sched_barrier(0);
+            // the waves read 16-byte pieces of the same 128-byte code lines;
+            // kept within a stage of each other they find the lines still
+            // in the L2 (no wait for memory here: loads stay in flight)
+            asm volatile("s_barrier" ::: "memory");
         }
     }
 
