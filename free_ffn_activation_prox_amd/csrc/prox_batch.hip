@@ -606,6 +606,9 @@ __global__ void __launch_bounds__(256) k_gateup_batch(GuArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             load(s0 + i + PD, ring[i]);
             __builtin_amdgcn_sched_barrier(0);
+            // the 4 waves request adjacent 128-byte pieces of the same rows:
+            // kept within a stage of each other (loads stay in flight)
+            asm volatile("s_barrier" ::: "memory");
         }
     }
     // the 4 waves' K quarters, one M-tile at a time: channel j0 + 16 mt + 4 q4 + i, token 16 g + r
