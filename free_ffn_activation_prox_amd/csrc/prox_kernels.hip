@@ -1763,9 +1763,50 @@ __global__ void __launch_bounds__(256) k_reduce_y(const float* __restrict__ ypar
     }
 }
 
+// The same sum for at most 32 partials (the matrix-core path's channel
+// slices): block 256 = 64 column quads (256 columns) x 4 partial groups;
+// thread (g = wave, q) sums partials g, g + 4, ... of quad q (every load in
+// flight, each wave instruction one contiguous kilobyte of a partial), then
+// the 4 groups are added through LDS in order.  One block per 256 columns
+// and token instead of per 16, so a batch of tokens is one round of blocks.
+constexpr int kRedFewMax = 32;
+__global__ void __launch_bounds__(256) k_reduce_y_few(const float* __restrict__ ypart, int d, int W2,
+                                                      float* __restrict__ y) {
+    __shared__ float4 acc[4][64];
+    const int b = blockIdx.y, t = threadIdx.x;
+    const int q = t & 63, g = t >> 6;
+    const int col = (blockIdx.x * 64 + q) * 4;
+    const bool in = col < d;                       // d % 8 == 0: a quad is all in or all out
+    const float* src = ypart + (size_t)b * W2 * d + (in ? col : 0);
+    float4 v[kRedFewMax / 4];
+#pragma unroll
+    for (int u = 0; u < kRedFewMax / 4; ++u) {
+        const int wv = g + 4 * u;
+        v[u] = in && wv < W2 ? *reinterpret_cast<const float4*>(src + (size_t)wv * d) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float4 s4 = v[0];
+#pragma unroll
+    for (int u = 1; u < kRedFewMax / 4; ++u) {
+        s4.x += v[u].x; s4.y += v[u].y; s4.z += v[u].z; s4.w += v[u].w;
+    }
+    acc[g][q] = s4;
+    __syncthreads();
+    if (g == 0 && in) {
+        float4 r = acc[0][q];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+            const float4 o = acc[i][q];
+            r.x += o.x; r.y += o.y; r.z += o.z; r.w += o.w;
+        }
+        *reinterpret_cast<float4*>(y + (size_t)b * d + col) = r;
+    }
+}
+
 hipError_t launch_reduce_y(const float* ypart, int B, int d, int W2, float* y, hipStream_t s) {
-    launch_kernel(k_reduce_y, dim3((d + kRedCols - 1) / kRedCols, B), dim3(256), 0, s, ypart, d,
-                       W2, y);
+    if (W2 <= kRedFewMax)
+        launch_kernel(k_reduce_y_few, dim3((d + 255) / 256, B), dim3(256), 0, s, ypart, d, W2, y);
+    else
+        launch_kernel(k_reduce_y, dim3((d + kRedCols - 1) / kRedCols, B), dim3(256), 0, s, ypart, d, W2, y);
     return hipGetLastError();
 }
 
